@@ -1,0 +1,242 @@
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+One step = one forward pass (S = scale Q K^T, online softmax, P V, LSE) and one backward pass
+(D pre-pass, dK/dV, dQ) over one batch of seeded synthetic input of the chosen workload, inputs
+resident in device memory.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+
+FLOP convention: forward 4*B*H*N^2*d (halved for causal; block-sparse counts active 128x128
+blocks), backward 2.5x forward.  value = (forward + backward flops) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 flop/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s (bf16, d=64/128) and % of MI355X MFMA peak"
+CSRC = os.path.join(ROOT, "exact_io_aware_flash_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def csrc_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def kernel_flops(w, block_mask):
+    import workloads
+
+    f = workloads.flops_fwd(w.B, w.H, w.N, w.d, w.causal, block_mask)
+    return {
+        # MFMA work each kernel performs by definition: fwd S and PV; dK/dV kernel recomputes S,
+        # computes dP, dV, dK; dQ kernel recomputes S and dP, computes dQ.
+        "fwd": f,
+        "bwd_dkdv": 2.0 * f,
+        "bwd_dq": 1.5 * f,
+    }
+
+
+def delta_bytes(w):
+    return 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current
+    kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_sha256") != csrc_digest():
+        return None
+    for k in rec.get("kernels", []):
+        if k.get("kernel") == kernel and k.get("workload") == workload:
+            return k.get("hbm_bytes_per_launch")
+    return None
+
+
+def cpu_baseline(w, t, heads: int):
+    """The fp64 oracle timed on the host on `heads` heads of the same inputs (forward + backward)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    f = lambda name, b, h: workloads.bf16_bits_to_f32(getattr(t, name)[b, h]).astype(np.float64)
+    t0 = time.perf_counter()
+    for i in range(heads):
+        b, h = divmod(i, w.H)
+        q, k, v, do = f("q", b, h), f("k", b, h), f("v", b, h), f("do", b, h)
+        oracle.forward_head(q, k, v, w.scale, w.causal, t.block_mask)
+        if not w.fwd_only:
+            oracle.backward_head(q, k, v, do, w.scale, w.causal, t.block_mask)
+    dt = time.perf_counter() - t0
+    one = workloads.flops_fwd(1, 1, w.N, w.d, w.causal, t.block_mask)
+    flops = heads * (one if w.fwd_only else 3.5 * one)
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} heads (b,h)=(0,0).. of the same workload, fp64 numpy "
+                  f"{'forward' if w.fwd_only else 'forward+backward'}, {dt:.1f} s, {cpu}",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "heads are independent, so the multi-GPU figure is the one-GPU figure on each GPU's share "
+              "of B*H.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    t = workloads.make(w, with_do=not w.fwd_only)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(t.q), to_dev(t.k), to_dev(t.v)
+    do = to_dev(t.do) if not w.fwd_only else None
+    mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f}s: {w.description}", file=sys.stderr, flush=True)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if not w.fwd_only:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    names = ["fwd"] if w.fwd_only else ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev):
+        # torch.cuda.Event records on torch's current stream, which is the stream every call below
+        # hands to the library, so each pair of events brackets exactly one kernel launch
+        if ev:
+            ev[0].record()
+        fa.fwd(q, k, v, w.scale, w.causal, mask, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        if w.fwd_only:
+            return
+        fa.bwd_preprocess(o, do, delta)
+        if ev:
+            ev[2].record()
+        fa.bwd_dkdv(q, k, v, do, lse, delta, w.scale, w.causal, mask, dk, dv)
+        if ev:
+            ev[3].record()
+        fa.bwd_dq(q, k, v, do, lse, delta, w.scale, w.causal, mask, dq)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
+    gpu_ms = sum(kern_ms.values())
+
+    ff = workloads.flops_fwd(B, H, N, d, w.causal, t.block_mask)
+    fb = 0.0 if w.fwd_only else 2.5 * ff
+    value = (ff + fb) / (ms_per_step * 1e-3) / 1e12
+    kf = kernel_flops(w, t.block_mask)
+    kernels = {}
+    for n in names:
+        ms = kern_ms[n]
+        if n == "bwd_preprocess":
+            kernels[n] = {"ms": ms, "GB/s": delta_bytes(w) / (ms * 1e-3) / 1e9}
+        else:
+            tf = kf[n] / (ms * 1e-3) / 1e12
+            kernels[n] = {"ms": ms, "TFLOP/s": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+    dom = max(names, key=lambda n: kern_ms[n])
+    if dom == "bwd_preprocess":
+        ach = delta_bytes(w) / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(dom, w.name)}
+    else:
+        ach = kf[dom] / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_for(dom, w.name)}
+    fwd_tf = ff / (kern_ms["fwd"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "block_sparse": w.sparse, "pass": "forward" if w.fwd_only else "forward+backward"},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "fwd_TFLOP/s": fwd_tf,
+        "fwd_frac_of_peak": fwd_tf / PEAK_BF16_TFLOPS,
+        "bwd_TFLOP/s": (fb / (sum(kern_ms[n] for n in names[1:]) * 1e-3) / 1e12) if not w.fwd_only else None,
+        "gpu_ms_per_step": gpu_ms,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

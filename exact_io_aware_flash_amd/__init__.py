@@ -1,0 +1,233 @@
+"""Exact tiled attention with online softmax for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in include/flash_attn.h: it checks tensor
+properties, allocates outputs with PyTorch, and passes raw device pointers and the current HIP
+stream to libflash_attn.so.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback path.  If the library has not been built this module raises on use.
+
+Build the library with `python -m exact_io_aware_flash_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflash_attn.so")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEADDIM = 3
+FA_ERR_ALIGN = 4
+FA_ERR_SCALE = 5
+FA_ERR_WORKSPACE = 6
+FA_ERR_HIP = 7
+FA_ERR_ALIAS = 8
+FA_ERR_FLAG = 9
+MASK_BLOCK = 128
+
+_lib = None
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflash_attn.so (raises if it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m exact_io_aware_flash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_fwd.restype = i
+    L.flash_attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_fwd_f32.restype = i
+    L.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.flash_attn_bwd_workspace_bytes.restype = sz
+    L.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd.restype = i
+    L.flash_attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_f32.restype = i
+    L.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.flash_attn_bwd_preprocess.restype = i
+    L.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_dkdv.restype = i
+    L.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_dq.restype = i
+    L.flash_attn_status_string.argtypes = [i]
+    L.flash_attn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().flash_attn_status_string(status).decode()
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().flash_attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name}: expected a tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _mask_arg(block_mask, N, device):
+    if block_mask is None:
+        return None
+    import torch
+
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    _check(block_mask, "block_mask", torch.uint8, (nb, nb), device)
+    return block_mask
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_mask=None, out=None, lse=None,
+        stream=None):
+    """Forward pass.  q, k, v: [B, H, N, d] bf16 or float32 CUDA tensors (same dtype).
+    block_mask: optional uint8 [nb, nb] CUDA tensor, nb = ceil(N / 128).
+    Returns (o [B, H, N, d] in the input dtype, lse [B, H, N] float32, natural log)."""
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(out, "out", q.dtype, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    bm = _mask_arg(block_mask, N, dev)
+    L = lib()
+    if q.dtype == torch.bfloat16:
+        fn, where = L.flash_attn_fwd, "flash_attn_fwd"
+    elif q.dtype == torch.float32:
+        fn, where = L.flash_attn_fwd_f32, "flash_attn_fwd_f32"
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)), _ptr(bm),
+            _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, where)
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, block_mask=None, dq=None, dk=None,
+        dv=None, workspace=None, stream=None):
+    """Backward pass for the forward call with the same q, k, v, scale, causal and block_mask.
+    Returns (dq, dk, dv) in the input dtype."""
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    need = workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    bm = _mask_arg(block_mask, N, dev)
+    L = lib()
+    if q.dtype == torch.bfloat16:
+        fn, where = L.flash_attn_bwd, "flash_attn_bwd"
+    elif q.dtype == torch.float32:
+        fn, where = L.flash_attn_bwd_f32, "flash_attn_bwd_f32"
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), B, H, N, d, scale, int(bool(causal)), _ptr(bm),
+            _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, where)
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------------------------
+# The three backward stages one by one (bf16).  Enqueued in this order they equal bwd().
+def bwd_preprocess(o, do, delta=None, stream=None):
+    """delta[b, h, i] = sum_c do * o (float32 [B, H, N])."""
+    import torch
+
+    B, H, N, d = o.shape
+    _check(o, "o", torch.bfloat16, (B, H, N, d), o.device)
+    _check(do, "do", torch.bfloat16, (B, H, N, d), o.device)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
+    _check(delta, "delta", torch.float32, (B, H, N), o.device)
+    st = lib().flash_attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_preprocess")
+    return delta
+
+
+def bwd_dkdv(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None, dk=None, dv=None, stream=None):
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    _check(delta, "delta", torch.float32, (B, H, N), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+                                   B, H, N, d, scale, int(bool(causal)), _ptr(bm), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_dkdv")
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None, dq=None, stream=None):
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    _check(delta, "delta", torch.float32, (B, H, N), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq), B, H, N, d,
+                                 scale, int(bool(causal)), _ptr(bm), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_dq")
+    return dq

@@ -1,0 +1,324 @@
+// C ABI of the attention library: argument validation on the host, then kernel launches.
+// Every check runs before the first HIP call, so an invalid call enqueues nothing and touches
+// no output (and can be exercised on a machine without a GPU).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/flash_attn.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr long long kMaxElems = (1LL << 62);
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask, bool bf16,
+                 long long* elems) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 30)) return FA_ERR_SHAPE;
+  const long long e = bh * N * d;
+  if (e <= 0 || e >= kMaxElems / 4) return FA_ERR_SHAPE;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  if (block_mask && bf16 && nb > FA_MAX_MASK_BLOCKS) return FA_ERR_SHAPE;
+  if (!bf16 && bh > 65535) return FA_ERR_SHAPE;  // the fp32 kernels put B*H on grid.y
+  const long long tiles = bh * ((N + 127) / 128);
+  if (tiles > 0x7fffffffLL) return FA_ERR_SHAPE;
+  *elems = e;
+  return FA_OK;
+}
+
+Range rng(const void* p, long long bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes};
+}
+
+// outputs must not overlap inputs or each other
+int check_alias(const Range* in, int nin, const Range* out, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(out[i], in[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+size_t workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  const size_t b = (size_t)B * H * N * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+template <typename T>
+int fwd_checked(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d, float scale,
+                int causal, const uint8_t* block_mask, bool bf16, long long* elems) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, block_mask, bf16, elems);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const long long tb = *elems * (long long)sizeof(T), lb = (long long)B * H * N * 4;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[4] = {rng(q, tb), rng(k, tb), rng(v, tb), rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[2] = {rng(o, tb), rng(lse, lb)};
+  return check_alias(in, 4, out, 2);
+}
+
+template <typename T>
+int bwd_checked(const T* q, const T* k, const T* v, const T* o, const T* dout, const float* lse, T* dq, T* dk, T* dv,
+                void* ws, size_t ws_bytes, int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, bool bf16, long long* elems) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, block_mask, bf16, elems);
+  if (st != FA_OK) return st;
+  if (!ws || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const long long tb = *elems * (long long)sizeof(T), lb = (long long)B * H * N * 4;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[7] = {rng(q, tb),    rng(k, tb),   rng(v, tb), rng(o, tb), rng(dout, tb), rng(lse, lb),
+                 rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[4] = {rng(dq, tb), rng(dk, tb), rng(dv, tb), rng(ws, (long long)workspace_bytes(B, H, N))};
+  return check_alias(in, 7, out, 4);
+}
+
+// Shared checks for the bf16 backward stages: all pointers non-null and aligned, shapes and
+// flags valid, outputs disjoint from inputs and from each other.
+int stage_checked(const void* const* in, const long long* in_bytes, int nin, void* const* out,
+                  const long long* out_bytes, int nout, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* block_mask) {
+  for (int i = 0; i < nin; ++i)
+    if (!in[i]) return FA_ERR_NULL;
+  for (int i = 0; i < nout; ++i)
+    if (!out[i]) return FA_ERR_NULL;
+  long long elems = 0;
+  int st = check_common(B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  for (int i = 0; i < nin; ++i)
+    if (!aligned16(in[i])) return FA_ERR_ALIGN;
+  for (int i = 0; i < nout; ++i)
+    if (!aligned16(out[i])) return FA_ERR_ALIGN;
+  Range ri[9], ro[3];
+  for (int i = 0; i < nin; ++i) ri[i] = rng(in[i], in_bytes[i]);
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  ri[nin] = rng(block_mask, block_mask ? nb * nb : 0);
+  for (int i = 0; i < nout; ++i) ro[i] = rng(out[i], out_bytes[i]);
+  return check_alias(ri, nin + 1, ro, nout);
+}
+
+fa::BwdArgs stage_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, const float* delta, void* dq, void* dk, void* dv, int B, int H, int N,
+                       int d, float scale, int causal, const uint8_t* block_mask) {
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.delta = const_cast<float*>(delta);
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * fa::kLog2e;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1; sizes must fit; mask blocks <= limit)";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than flash_attn_bwd_workspace_bytes()";
+    case FA_ERR_HIP: return "a HIP kernel launch failed";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_FLAG: return "causal must be 0 or 1";
+    default: return "unknown status";
+  }
+}
+
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  return workspace_bytes(B, H, N);
+}
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  long long elems = 0;
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const __bf16* vb = static_cast<const __bf16*>(v);
+  __bf16* ob = static_cast<__bf16*>(o);
+  int st = fwd_checked(qb, kb, vb, ob, lse, B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = qb;
+  a.k = kb;
+  a.v = vb;
+  a.o = ob;
+  a.lse = lse;
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * fa::kLog2e;
+  return status_of(fa::launch_fwd_bf16(a, stream));
+}
+
+int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                       int d, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  long long elems = 0;
+  int st = fwd_checked(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, false, &elems);
+  if (st != FA_OK) return st;
+  fa::F32Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out_o = o;
+  a.lse = lse;
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  return status_of(fa::launch_fwd_f32(a, stream));
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes_, int B, int H, int N, int d,
+                   float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  long long elems = 0;
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  int st = bwd_checked(a.q, a.k, a.v, a.o, a.dout, lse, a.dq, a.dk, a.dv, workspace, workspace_bytes_, B, H, N, d,
+                       scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  a.delta = static_cast<float*>(workspace);
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * fa::kLog2e;
+  return status_of(fa::launch_bwd_bf16(a, stream));
+}
+
+int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
+                       const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes_,
+                       int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask,
+                       hipStream_t stream) {
+  long long elems = 0;
+  int st = bwd_checked(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes_, B, H, N, d, scale, causal,
+                       block_mask, false, &elems);
+  if (st != FA_OK) return st;
+  fa::F32Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = const_cast<float*>(lse);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  return status_of(fa::launch_bwd_f32(a, stream));
+}
+
+int flash_attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N, int d,
+                              hipStream_t stream) {
+  const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
+  const void* in[2] = {o, dout};
+  const long long ib[2] = {tb, tb};
+  void* out[1] = {delta};
+  const long long ob[1] = {rb};
+  int st = stage_checked(in, ib, 2, out, ob, 1, B, H, N, d, 1.0f, 0, nullptr);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = stage_args(nullptr, nullptr, nullptr, o, dout, nullptr, delta, nullptr, nullptr, nullptr,
+                                   B, H, N, d, 1.0f, 0, nullptr);
+  return status_of(fa::launch_bwd_delta_bf16(a, stream));
+}
+
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                        const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, hipStream_t stream) {
+  const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
+  const void* in[6] = {q, k, v, dout, lse, delta};
+  const long long ib[6] = {tb, tb, tb, tb, rb, rb};
+  void* out[2] = {dk, dv};
+  const long long ob[2] = {tb, tb};
+  int st = stage_checked(in, ib, 6, out, ob, 2, B, H, N, d, scale, causal, block_mask);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a =
+      stage_args(q, k, v, nullptr, dout, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, block_mask);
+  return status_of(fa::launch_bwd_dkdv_bf16(a, stream));
+}
+
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+                      const uint8_t* block_mask, hipStream_t stream) {
+  const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
+  const void* in[6] = {q, k, v, dout, lse, delta};
+  const long long ib[6] = {tb, tb, tb, tb, rb, rb};
+  void* out[1] = {dq};
+  const long long ob[1] = {tb};
+  int st = stage_checked(in, ib, 6, out, ob, 1, B, H, N, d, scale, causal, block_mask);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a =
+      stage_args(q, k, v, nullptr, dout, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, block_mask);
+  return status_of(fa::launch_bwd_dq_bf16(a, stream));
+}
+
+}  // extern "C"

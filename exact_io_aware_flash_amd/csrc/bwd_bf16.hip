@@ -1,0 +1,462 @@
+// Backward pass, bf16 inputs/outputs, fp32 accumulation, for gfx950.
+//
+// The pages keep only the per-row softmax statistic from the forward pass and recompute the
+// rest tile by tile ([P3] "How FlashAttention Eliminates Transformer Memory Bottlenecks",
+// "Innovation #3: Strategic recomputation in the backward pass").  With LSE saved,
+// P = exp(scale Q K^T - LSE) needs no running maximum.  Gradients of L = sum(O * dO):
+//   D = rowsum(dO * O)            (pre-pass; equals rowsum(P * dP))
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Three kernels on one stream:
+//  1. bwd_delta:  D per row (bandwidth-bound, 16-byte loads, shuffle reduction).
+//  2. bwd_dkdv:   one workgroup per (b*h, 128-key block): 4 waves x 32 keys.  K and V of the
+//                 wave's keys stay in registers as MFMA B operands; Q, dO, LSE, D tiles of 64
+//                 rows stream through double-buffered LDS.  S = Q K^T puts one key per lane and
+//                 16 queries in registers, which is the A-operand shape of dV = P^T dO and
+//                 dK = dS^T Q; their B operands (dO and Q with queries as the contraction index)
+//                 come from the same LDS tiles through transposed reads.
+//  3. bwd_dq:     one workgroup per (b*h, 128-query block), K/V tiles double-buffered in LDS:
+//                 S^T = K Q^T and dP^T = V dO^T give one query per lane (the B-operand shape of
+//                 dQ^T = K^T dS^T); K^T is read transposed from the K tile.
+// dQ is produced without atomics, so every output element is written once and results are
+// bitwise reproducible run to run.
+#include "fa_common.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+// ------------------------------------------------------------------------------------------ D
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                        float* __restrict__ delta, long rows) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int TPR = D / EPL;         // threads per row (power of two)
+  constexpr int RPB = 256 / TPR;
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 ov = *reinterpret_cast<const uint4*>(o + row * D + part * EPL);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dout + row * D + part * EPL);
+    const T* op = reinterpret_cast<const T*>(&ov);
+    const T* dp = reinterpret_cast<const T*>(&dv);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc += (float)op[e] * (float)dp[e];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
+  constexpr int BKV = 128, BQ = 64;
+  constexpr int DC = D / 16, DB = D / 32;
+  constexpr int TILE_BYTES = BQ * D * 2;
+  constexpr int CH = TILE_BYTES / 16 / 256;
+  constexpr int CPR = D / 8;
+
+  __shared__ __attribute__((aligned(16))) char lds_q[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_do[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_l[2][BQ];
+  __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];
+  __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int bcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+  const int N = a.N;
+  int bh, kt;
+  sched_decode(sc, gridDim.x, bh, kt);
+  const int k0 = kt * BKV;
+  const int k0w = k0 + 32 * w;
+  const size_t base = (size_t)bh * N * D;
+  const size_t rbase = (size_t)bh * N;
+
+  // ---- query tiles that see this key block
+  const int nqt = (N + BQ - 1) / BQ;
+  int q_first = 0, ntiles = nqt;
+  if (CAUSAL) {
+    q_first = k0 / BQ;
+    ntiles = nqt - q_first;
+  }
+  if (SPARSE) {
+    if (w == 0) {
+      const int cnt = build_block_list(a.mask, a.nb, kt, true, CAUSAL ? kt : 0, a.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = bcount;
+    ntiles = 2 * cnt;
+    if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BQ >= N) ntiles -= 1;
+  }
+  auto tile_start = [&](int t) -> int {
+    if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BQ;
+    return (q_first + t) * BQ;
+  };
+
+  // ---- this lane's key: K and V rows as B operands
+  const int key = k0w + c32;
+  bf16x8 kreg[DC], vreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    if (key < N) {
+      kreg[c] = *reinterpret_cast<const bf16x8*>(a.k + base + (size_t)key * D + 16 * c + 8 * h);
+      vreg[c] = *reinterpret_cast<const bf16x8*>(a.v + base + (size_t)key * D + 16 * c + 8 * h);
+    } else {
+      kreg[c] = zero_bf16x8();
+      vreg[c] = zero_bf16x8();
+    }
+  }
+  f32x16 dvacc[DB], dkacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dvacc[i] = zero16();
+    dkacc[i] = zero16();
+  }
+  const float sl = a.scale_log2;
+
+  uint4 qpre[CH], dpre[CH];
+  float lpre = 0.f, dlpre = 0.f;
+  auto gload = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      const int qr = q0 + row;
+      if (qr < N) {
+        qpre[i] = *reinterpret_cast<const uint4*>(a.q + base + (size_t)qr * D + col);
+        dpre[i] = *reinterpret_cast<const uint4*>(a.dout + base + (size_t)qr * D + col);
+      } else {
+        qpre[i] = make_uint4(0, 0, 0, 0);
+        dpre[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < BQ) {
+      const int qr = q0 + tid;
+      // rows past N, or rows that see no key, get +inf so that P = 0
+      const float l = qr < N ? a.lse[rbase + qr] : neg_inf();
+      lpre = (l == neg_inf()) ? __builtin_huge_valf() : l * kLog2e;
+      dlpre = qr < N ? a.delta[rbase + qr] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(lds_q[buf] + lds_off<D>(row, col)) = qpre[i];
+      *reinterpret_cast<uint4*>(lds_do[buf] + lds_off<D>(row, col)) = dpre[i];
+    }
+    if (tid < BQ) {
+      lds_l[buf][tid] = lpre;
+      lds_d[buf][tid] = dlpre;
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(tile_start(0));
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int q0 = tile_start(t);
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) gload(tile_start(t + 1));
+    const char* tq = lds_q[buf];
+    const char* tdo = lds_do[buf];
+
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int qs = q0 + 32 * s;
+      if (qs >= N) continue;
+      if (CAUSAL && qs + 31 < k0w) continue;  // every query of this step precedes every key of the wave
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        sacc = mfma32(lds_row8<D>(tq, 32 * s + c32, 16 * c + 8 * h), kreg[c], sacc);
+        pacc = mfma32(lds_row8<D>(tdo, 32 * s + c32, 16 * c + 8 * h), vreg[c], pacc);
+      }
+      // rows of this lane's accumulators: query 32 s + 8 g + 4 h + e in register 4 g + e
+      const bool need_mask = (k0w + 32 > N) || (CAUSAL && qs < k0w + 31);
+      bf16x8 pp[2], dsp[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_l[buf][32 * s + 8 * g + 4 * h]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_d[buf][32 * s + 8 * g + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -l4[e]));
+          if (need_mask) {
+            const int qi = qs + 8 * g + 4 * h + e;
+            if (key >= N || (CAUSAL && key > qi)) p = 0.f;
+          }
+          const float ds = p * (pacc[r] - d4[e]);
+          pp[r >> 3][r & 7] = (__bf16)p;
+          dsp[r >> 3][r & 7] = (__bf16)ds;
+        }
+      }
+      // dV += P^T dO ; dK += dS^T Q   (contraction over the 32 queries, two chunks of 16)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          dvacc[db] = mfma32(pp[mm], lds_tr_operand<D>(tdo, 32 * s + 16 * mm, 32 * db, lane), dvacc[db]);
+          dkacc[db] = mfma32(dsp[mm], lds_tr_operand<D>(tq, 32 * s + 16 * mm, 32 * db, lane), dkacc[db]);
+        }
+    }
+
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds dims 32 db + c32 of keys k0w + 8 g + 4 h + e
+  const float scale = a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = k0w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (kr < N) {
+        const size_t off = base + (size_t)kr * D + 32 * db + c32;
+        a.dv[off] = (__bf16)dvacc[db][r];
+        a.dk[off] = (__bf16)(dkacc[db][r] * scale);
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------ dQ
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a, Sched sc) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int DC = D / 16, DB = D / 32;
+  constexpr int TILE_BYTES = BC * D * 2;
+  constexpr int CH = TILE_BYTES / 16 / 256;
+  constexpr int CPR = D / 8;
+
+  __shared__ __attribute__((aligned(16))) char lds_k[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][TILE_BYTES];
+  __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int bcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+  const int N = a.N;
+  int bh, qt;
+  sched_decode(sc, gridDim.x, bh, qt);
+  const int q0 = qt * BR;
+  const size_t base = (size_t)bh * N * D;
+  const size_t rbase = (size_t)bh * N;
+
+  const int nk = (N + BC - 1) / BC;
+  int ntiles = nk;
+  if (CAUSAL) ntiles = min(nk, (min(q0 + BR, N) - 1) / BC + 1);
+  if (SPARSE) {
+    const int qb = q0 / kMaskBlock;
+    if (w == 0) {
+      const int cnt = build_block_list(a.mask, a.nb, qb, false, 0, CAUSAL ? qb + 1 : a.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = bcount;
+    ntiles = 2 * cnt;
+    if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BC >= N) ntiles -= 1;
+  }
+  auto tile_start = [&](int t) -> int {
+    if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
+    return t * BC;
+  };
+
+  const int qrow = q0 + 32 * w + c32;
+  bf16x8 qreg[DC], doreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    if (qrow < N) {
+      qreg[c] = *reinterpret_cast<const bf16x8*>(a.q + base + (size_t)qrow * D + 16 * c + 8 * h);
+      doreg[c] = *reinterpret_cast<const bf16x8*>(a.dout + base + (size_t)qrow * D + 16 * c + 8 * h);
+    } else {
+      qreg[c] = zero_bf16x8();
+      doreg[c] = zero_bf16x8();
+    }
+  }
+  float lse2 = __builtin_huge_valf(), dval = 0.f;
+  if (qrow < N) {
+    const float l = a.lse[rbase + qrow];
+    lse2 = (l == neg_inf()) ? __builtin_huge_valf() : l * kLog2e;
+    dval = a.delta[rbase + qrow];
+  }
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
+  const float sl = a.scale_log2;
+
+  uint4 kpre[CH], vpre[CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      const int kr = k0 + row;
+      if (kr < N) {
+        kpre[i] = *reinterpret_cast<const uint4*>(a.k + base + (size_t)kr * D + col);
+        vpre[i] = *reinterpret_cast<const uint4*>(a.v + base + (size_t)kr * D + col);
+      } else {
+        kpre[i] = make_uint4(0, 0, 0, 0);
+        vpre[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(lds_k[buf] + lds_off<D>(row, col)) = kpre[i];
+      *reinterpret_cast<uint4*>(lds_v[buf] + lds_off<D>(row, col)) = vpre[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(tile_start(0));
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int k0 = tile_start(t);
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) gload(tile_start(t + 1));
+    const char* tk = lds_k[buf];
+    const char* tv = lds_v[buf];
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w);
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (CAUSAL && k0 + 32 * kb > q0 + 32 * w + 31) continue;  // every key of the block follows every query of the wave
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        sacc = mfma32(lds_row8<D>(tk, 32 * kb + c32, 16 * c + 8 * h), qreg[c], sacc);
+        pacc = mfma32(lds_row8<D>(tv, 32 * kb + c32, 16 * c + 8 * h), doreg[c], pacc);
+      }
+      bf16x8 dsp[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lse2));
+        if (need_mask) {
+          const int kr = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kr >= N || (CAUSAL && kr > qrow)) p = 0.f;
+        }
+        dsp[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dval));
+      }
+      // dQ^T += K^T dS^T (contraction over the 32 keys of the block)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+          dqacc[db] = mfma32(lds_tr_operand<D>(tk, 32 * kb + 16 * m2, 32 * db, lane), dsp[m2], dqacc[db]);
+    }
+
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+    __bf16* row = a.dq + base + (size_t)qrow * D;
+    const float scale = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dqacc[db][4 * g + e] * scale);
+        *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * g + 4 * h) = v4;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
+  const long rows = (long)a.BH * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_delta_kernel<__bf16, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o,
+                     a.dout, a.delta, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool C, bool S>
+hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
+  const int nkv = (a.N + 127) / 128;
+  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc);
+  return hipGetLastError();
+}
+
+template <int D, bool C, bool S>
+hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
+  const int nq = (a.N + 127) / 128;
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
+  return hipGetLastError();
+}
+
+// dispatch on (d, causal, sparse) to a kernel template instantiation
+template <template <int, bool, bool> class L>
+hipError_t dispatch(const BwdArgs& a, hipStream_t st) {
+  const bool c = a.causal != 0, s = a.mask != nullptr;
+  if (a.d == 64) {
+    if (c) return s ? L<64, true, true>::run(a, st) : L<64, true, false>::run(a, st);
+    return s ? L<64, false, true>::run(a, st) : L<64, false, false>::run(a, st);
+  }
+  if (c) return s ? L<128, true, true>::run(a, st) : L<128, true, false>::run(a, st);
+  return s ? L<128, false, true>::run(a, st) : L<128, false, false>::run(a, st);
+}
+
+template <int D, bool C, bool S>
+struct DkdvL {
+  static hipError_t run(const BwdArgs& a, hipStream_t st) { return launch_dkdv_t<D, C, S>(a, st); }
+};
+template <int D, bool C, bool S>
+struct DqL {
+  static hipError_t run(const BwdArgs& a, hipStream_t st) { return launch_dq_t<D, C, S>(a, st); }
+};
+
+}  // namespace
+
+hipError_t launch_bwd_delta_bf16(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch_delta_t<64>(a, stream) : launch_delta_t<128>(a, stream);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream) { return dispatch<DkdvL>(a, stream); }
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream) { return dispatch<DqL>(a, stream); }
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = launch_bwd_delta_bf16(a, stream);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv_bf16(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_bf16(a, stream);
+}
+
+// The fp32 path shares the D pre-pass kernel.
+hipError_t launch_delta_f32(const float* o, const float* dout, float* delta, long rows, int d, hipStream_t st) {
+  if (d == 64) {
+    constexpr int RPB = 256 / (64 / 4);
+    hipLaunchKernelGGL((bwd_delta_kernel<float, 64>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, o,
+                       dout, delta, rows);
+  } else {
+    constexpr int RPB = 256 / (128 / 4);
+    hipLaunchKernelGGL((bwd_delta_kernel<float, 128>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, o,
+                       dout, delta, rows);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

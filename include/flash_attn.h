@@ -1,0 +1,148 @@
+/*
+ * flash_attn.h — C ABI of an exact tiled scaled-dot-product attention library for AMD MI355X
+ * (gfx950).  Forward: S = scale * Q K^T, row softmax and P V fused tile by tile with an online
+ * softmax, the N x N score matrix never written to device memory, one log-sum-exp per row
+ * returned.  Backward: S and P recomputed tile by tile from that log-sum-exp.
+ *
+ * Sources (web pages on the method):
+ *   [P2] "FlashAttention: how a memory trick unlocked today's giant AI models" (khetwal.com)
+ *   [P3] "How FlashAttention Eliminates Transformer Memory Bottlenecks" (Galileo blog)
+ *
+ * Conventions shared by every entry point
+ *   Layout      Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d] tensors (one
+ *               N x d matrix per batch b and head h, as in [P2 "A Worked Example in Pseudocode"]).
+ *               LSE is a contiguous [B, H, N] float32 tensor.  All are device pointers, 16-byte
+ *               aligned.  Offsets are computed in 64 bits.
+ *   Scale       S = scale * Q K^T; scale must be finite and > 0 (usually 1/sqrt(d)).
+ *   Causal      causal = 1 lets query i see key j only when j <= i (square, top-left aligned);
+ *               causal = 0 lets every query see every key.
+ *   Block mask  block_mask == NULL means dense.  Otherwise a device uint8 array [nb][nb],
+ *               nb = ceil(N / 128), row-major, shared by every (b, h): query block I may see key
+ *               block J iff block_mask[I * nb + J] != 0.  Masked 128 x 128 tiles are skipped,
+ *               never computed ([P3 "Innovation #5: Extension to block-sparse attention
+ *               patterns"]).  It combines with causal by AND.  The bf16 entry points accept
+ *               nb <= FA_MAX_MASK_BLOCKS.
+ *   Dead rows   a query that sees no key gets O = 0, LSE = -inf and contributes no gradient.
+ *   Ownership   the caller owns every buffer (including the backward workspace).  The library
+ *               allocates no device memory, keeps no state between calls and may be called from
+ *               several host threads.  Inputs are read-only and may alias one another; outputs
+ *               must not overlap any input or each other (checked: FA_ERR_ALIAS).
+ *   Asynchrony  work is enqueued on `stream` (NULL = the default stream) and the call returns
+ *               without waiting; results are visible after the stream is synchronised.
+ *   Errors      arguments are checked on the host first; on any FA_ERR_* other than FA_ERR_HIP
+ *               nothing is enqueued and no output is touched.  FA_ERR_HIP reports a failed
+ *               launch (hipGetLastError); some kernels may already be enqueued.  NaN/Inf inside
+ *               the inputs are not checked; they propagate to the affected rows.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_MASK_BLOCK 128
+#define FA_MAX_MASK_BLOCKS 2048
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, a size overflows, or nb > FA_MAX_MASK_BLOCKS */
+  FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 5,     /* scale not finite or not > 0 */
+  FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than flash_attn_bwd_workspace_bytes() */
+  FA_ERR_HIP = 7,       /* a kernel launch failed */
+  FA_ERR_ALIAS = 8,     /* an output overlaps an input or another output */
+  FA_ERR_FLAG = 9       /* causal not 0 or 1 */
+};
+
+/* Forward, bf16 inputs and outputs, fp32 accumulation.
+ * Computes, per (b, h), O = softmax(scale * Q K^T restricted to visible keys) V and
+ * LSE_i = ln sum_j exp(scale * q_i . k_j) over the visible keys j (natural log).
+ * Definition: [P2 "The Quadratic Memory Bottleneck"] (S, P, O); tiling and online softmax:
+ * [P2 "Tiling: Breaking the Problem into Pieces", "The Trick: Online Softmax"]; the row
+ * statistic kept for the backward pass: [P3 "Innovation #3: Strategic recomputation in the
+ * backward pass"].
+ *   q, k, v  in   bf16 [B, H, N, d]
+ *   o        out  bf16 [B, H, N, d] (round to nearest even)
+ *   lse      out  float32 [B, H, N]
+ */
+int flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t *block_mask, hipStream_t stream);
+
+/* Forward with float32 inputs, outputs and arithmetic (no reduced-precision products).
+ * Same definition and arguments as flash_attn_fwd with float tensors. */
+int flash_attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const uint8_t *block_mask, hipStream_t stream);
+
+/* Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for this shape (the
+ * per-row D = rowsum(dO * O) of the pre-pass, float32 [B, H, N], rounded up to 256 bytes).
+ * Returns 0 if B, H or N < 1. */
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward, bf16.  Gradients of L = sum(O * dO) with respect to q, k, v, recomputing S and P
+ * tile by tile from lse ([P3 "Innovation #3: Strategic recomputation in the backward pass"]):
+ *   D = rowsum(dO * O);  P = exp(scale * Q K^T - LSE);  dV = P^T dO;  dP = dO V^T;
+ *   dS = P * (dP - D);   dQ = scale dS K;   dK = scale dS^T Q.
+ *   q, k, v     in   bf16 [B, H, N, d]  (the forward's inputs)
+ *   o, lse      in   the forward's outputs for the same inputs, scale, causal and block_mask
+ *   dout        in   bf16 [B, H, N, d]  (dO)
+ *   dq, dk, dv  out  bf16 [B, H, N, d]
+ *   workspace   scratch of at least flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *               aligned; its contents are undefined afterwards.
+ */
+int flash_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse,
+                   void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t *block_mask, hipStream_t stream);
+
+/* Backward with float32 tensors and arithmetic; same definition and arguments. */
+int flash_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
+                       const float *dout, const float *lse,
+                       float *dq, float *dk, float *dv,
+                       void *workspace, size_t workspace_bytes,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const uint8_t *block_mask, hipStream_t stream);
+
+/* The three stages flash_attn_bwd runs, exposed one by one (bf16) for callers that schedule
+ * them themselves or time them separately.  Enqueued in this order on one stream they produce
+ * exactly what flash_attn_bwd produces.  Same conventions and checks as flash_attn_bwd; `delta`
+ * is a float32 [B, H, N] device tensor, 16-byte aligned.
+ *
+ * Stage 1: delta_i = sum_c dO_ic * O_ic (the D pre-pass; equals rowsum(P * dP)).
+ *   o, dout in bf16 [B, H, N, d]; delta out. */
+int flash_attn_bwd_preprocess(const void *o, const void *dout, float *delta,
+                              int B, int H, int N, int d, hipStream_t stream);
+
+/* Stage 2: dK and dV, one pass over the query tiles that see each key block
+ * (recomputing S and P from lse, [P3 "Innovation #3"]).
+ *   q, k, v, dout bf16 in; lse, delta float32 in; dk, dv bf16 out. */
+int flash_attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                        const float *lse, const float *delta, void *dk, void *dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const uint8_t *block_mask, hipStream_t stream);
+
+/* Stage 3: dQ, one pass over the key tiles each query block sees (recomputing S, P and dP).
+ *   q, k, v, dout bf16 in; lse, delta float32 in; dq bf16 out. */
+int flash_attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, const float *delta, void *dq,
+                      int B, int H, int N, int d, float scale, int causal,
+                      const uint8_t *block_mask, hipStream_t stream);
+
+/* Static English text for a status code ("unknown status" for anything else). */
+const char *flash_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function that
+include/*.h declares, and rejects invalid arguments with the documented status before touching
+the GPU (invalid calls return before the first HIP call, so dummy pointers are never used)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import exact_io_aware_flash_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_io_aware_flash_amd import build
+        build.build()
+    return fa.lib()
+
+
+def declared_functions():
+    names = []
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(flash_attn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_f32", "flash_attn_bwd_f32",
+              "flash_attn_bwd_workspace_bytes", "flash_attn_status_string", "flash_attn_bwd_preprocess",
+              "flash_attn_bwd_dkdv", "flash_attn_bwd_dq"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(L):
+    import exact_io_aware_flash_amd as fa
+    for code in range(0, 10):
+        s = fa.status_string(code)
+        assert s and s != "unknown status", code
+    assert fa.status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    import exact_io_aware_flash_amd as fa
+    assert fa.workspace_bytes(1, 1, 1, 64) == 256
+    assert fa.workspace_bytes(2, 3, 100, 128) == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert fa.workspace_bytes(0, 1, 1, 64) == 0
+
+
+# fake, 16-byte aligned, non-overlapping device addresses: never dereferenced by invalid calls
+BIG = 1 << 36
+
+
+def ptrs(n, start=1 << 40):
+    return [ctypes.c_void_p(start + i * BIG) for i in range(n)]
+
+
+def fwd_call(L, q, k, v, o, lse, B=1, H=1, N=128, d=64, scale=0.125, causal=0, mask=None, f32=False):
+    fn = L.flash_attn_fwd_f32 if f32 else L.flash_attn_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, scale, causal, mask, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_argument_errors(L, f32):
+    import exact_io_aware_flash_amd as fa
+    q, k, v, o, lse = ptrs(5)
+    assert fwd_call(L, None, k, v, o, lse, f32=f32) == fa.FA_ERR_NULL
+    assert fwd_call(L, q, k, v, o, None, f32=f32) == fa.FA_ERR_NULL
+    assert fwd_call(L, q, k, v, o, lse, N=0, f32=f32) == fa.FA_ERR_SHAPE
+    assert fwd_call(L, q, k, v, o, lse, B=0, f32=f32) == fa.FA_ERR_SHAPE
+    assert fwd_call(L, q, k, v, o, lse, H=-1, f32=f32) == fa.FA_ERR_SHAPE
+    for d in (0, 32, 96, 256):
+        assert fwd_call(L, q, k, v, o, lse, d=d, f32=f32) == fa.FA_ERR_HEADDIM
+    for s in (0.0, -0.5, float("inf"), float("nan")):
+        assert fwd_call(L, q, k, v, o, lse, scale=s, f32=f32) == fa.FA_ERR_SCALE
+    assert fwd_call(L, q, k, v, o, lse, causal=2, f32=f32) == fa.FA_ERR_FLAG
+    mis = ctypes.c_void_p(q.value + 8)
+    assert fwd_call(L, mis, k, v, o, lse, f32=f32) == fa.FA_ERR_ALIGN
+    # outputs aliasing inputs or each other
+    assert fwd_call(L, q, k, v, q, lse, f32=f32) == fa.FA_ERR_ALIAS
+    assert fwd_call(L, q, k, v, o, ctypes.c_void_p(o.value + 64), f32=f32) == fa.FA_ERR_ALIAS
+
+
+def test_fwd_mask_limit(L):
+    import exact_io_aware_flash_amd as fa
+    q, k, v, o, lse, m = ptrs(6)
+    N = (2048 + 1) * 128
+    assert fwd_call(L, q, k, v, o, lse, N=N, mask=m) == fa.FA_ERR_SHAPE
+
+
+def bwd_call(L, p, ws, ws_bytes, B=1, H=1, N=128, d=64, scale=0.125, causal=0, mask=None, f32=False):
+    fn = L.flash_attn_bwd_f32 if f32 else L.flash_attn_bwd
+    return fn(*p, ws, ws_bytes, B, H, N, d, scale, causal, mask, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_bwd_argument_errors(L, f32):
+    import exact_io_aware_flash_amd as fa
+    p = ptrs(9)
+    ws = ptrs(1, start=1 << 45)[0]
+    need = fa.workspace_bytes(1, 1, 128, 64)
+    assert bwd_call(L, p, None, need, f32=f32) == fa.FA_ERR_WORKSPACE
+    assert bwd_call(L, p, ws, need - 1, f32=f32) == fa.FA_ERR_WORKSPACE
+    for i in range(9):
+        pp = list(p)
+        pp[i] = None
+        assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_NULL, i
+    assert bwd_call(L, p, ws, need, d=80, f32=f32) == fa.FA_ERR_HEADDIM
+    assert bwd_call(L, p, ws, need, scale=-1.0, f32=f32) == fa.FA_ERR_SCALE
+    assert bwd_call(L, p, ws, need, causal=-1, f32=f32) == fa.FA_ERR_FLAG
+    pp = list(p)
+    pp[6] = pp[0]  # dq == q
+    assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_ALIAS
+    pp = list(p)
+    pp[7] = pp[8]  # dk == dv
+    assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_ALIAS
+    assert bwd_call(L, p, p[1], need, f32=f32) == fa.FA_ERR_ALIAS  # workspace over k
+    mis = ctypes.c_void_p(ws.value + 4)
+    assert bwd_call(L, p, mis, need, f32=f32) == fa.FA_ERR_ALIGN
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    import exact_io_aware_flash_amd as fa
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.lib()
+
+
+def test_stage_argument_errors(L):
+    import exact_io_aware_flash_amd as fa
+    q, k, v, do, lse, delta, dk, dv, o = ptrs(9)
+    dims = (1, 1, 128, 64)
+    assert L.flash_attn_bwd_preprocess(None, do, delta, *dims, None) == fa.FA_ERR_NULL
+    assert L.flash_attn_bwd_preprocess(o, do, delta, 1, 1, 128, 32, None) == fa.FA_ERR_HEADDIM
+    assert L.flash_attn_bwd_preprocess(o, do, ctypes.c_void_p(o.value + 16), *dims, None) == fa.FA_ERR_ALIAS
+    args = [q, k, v, do, lse, delta, dk, dv]
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_NULL, i
+    assert L.flash_attn_bwd_dkdv(*args, 1, 1, 0, 64, 0.125, 0, None, None) == fa.FA_ERR_SHAPE
+    assert L.flash_attn_bwd_dkdv(*args, *dims, 0.0, 0, None, None) == fa.FA_ERR_SCALE
+    a = list(args)
+    a[7] = a[6]
+    assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
+    a = list(args)
+    a[6] = a[4]  # dk over lse
+    assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
+    qargs = [q, k, v, do, lse, delta, dk]
+    assert L.flash_attn_bwd_dq(*qargs, *dims, 0.125, 3, None, None) == fa.FA_ERR_FLAG
+    a = list(qargs)
+    a[6] = ctypes.c_void_p(dk.value + 2)
+    assert L.flash_attn_bwd_dq(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIGN
+    a = list(qargs)
+    a[6] = a[0]
+    assert L.flash_attn_bwd_dq(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS

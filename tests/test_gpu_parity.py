@@ -1,0 +1,212 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element.
+
+Tolerances: max-abs 1e-5 for fp32 inputs, 2e-2 for bf16 inputs (fp32 accumulation; for bf16
+outputs with |ref| >= 8 half a bf16 ulp of the value is added, the output's own storage
+rounding), 1e-3 for LSE.  Full-size workloads are run on the device in full; the oracle checks
+sampled heads, rows and key columns of them.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+
+import workloads
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return G.device()
+
+
+def _run_and_compare(name, t, scale, causal, dev, heads, backward=True, rows=None, cols=None):
+    G.say(f"[case] {name}: shape={t.q.shape} dtype={t.dtype} causal={causal} "
+          f"mask={'yes' if t.block_mask is not None else 'no'} bwd={backward}")
+    t0 = time.time()
+    res = G.run_lib(t, scale, causal, dev, backward)
+    G.say(f"  device done in {time.time() - t0:.1f}s")
+    G.compare_heads(t, res, scale, causal, heads, backward, rows, cols)
+    return res
+
+
+# ------------------------------------------------------------------------------ the workloads
+def test_tiny_fp32_exact(dev):
+    w = workloads.WORKLOADS["tiny"]
+    t = workloads.make(w)
+    _run_and_compare("tiny fp32", t, w.scale, w.causal, dev, heads=[(0, 0)])
+
+
+def test_bert_shaped_full(dev):
+    w = workloads.WORKLOADS["bert"]
+    t = workloads.make(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _run_and_compare("bert", t, w.scale, w.causal, dev, heads)
+
+
+def test_gpt2_shaped_causal(dev):
+    w = workloads.WORKLOADS["gpt2"]
+    t = workloads.make(w)
+    _run_and_compare("gpt2", t, w.scale, w.causal, dev, heads=[(0, 0), (3, 7), (7, 11)])
+
+
+def test_long_context_causal_sampled(dev):
+    w = workloads.WORKLOADS["long"]
+    t = workloads.make(w)
+    rows = G.sample_rows(w.N, 48, seed=7)
+    cols = G.sample_rows(w.N, 24, seed=8)
+    _run_and_compare("long", t, w.scale, w.causal, dev, heads=[(0, 0), (0, 31)], rows=rows, cols=cols)
+
+
+def test_long_context_64k_forward_sampled(dev):
+    w = workloads.WORKLOADS["long64k"]
+    t = workloads.make(w, with_do=False)
+    rows = G.sample_rows(w.N, 48, seed=9)
+    _run_and_compare("long64k fwd", t, w.scale, w.causal, dev, heads=[(0, 0), (0, 7)], backward=False, rows=rows)
+
+
+def test_block_sparse(dev):
+    w = workloads.WORKLOADS["sparse"]
+    t = workloads.make(w)
+    _run_and_compare("sparse", t, w.scale, w.causal, dev, heads=[(0, 0), (3, 15)])
+
+
+# ------------------------------------------------------------------------------ sweeps and edges
+SMALL_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mode", ["dense", "causal", "mask", "causal+mask"])
+def test_small_n_sweep(dev, d, dtype, mode):
+    causal = "causal" in mode
+    for N in SMALL_N:
+        t = workloads.random_case(1, 2, N, d, dtype, seed=100 + N,
+                                  mask_density=0.6 if "mask" in mode else None, mask_seed=200 + N)
+        if t.block_mask is not None:
+            np.fill_diagonal(t.block_mask, 1)
+        _run_and_compare(f"sweep N={N} d={d} {dtype} {mode}", t, 1.0 / math.sqrt(d), causal, dev,
+                         heads=[(0, 0), (0, 1)])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_multi_tile(dev, d, causal):
+    t = workloads.random_case(2, 3, 1000, d, "bf16", seed=300 + d, mask_density=0.5, mask_seed=301)
+    np.fill_diagonal(t.block_mask, 1)
+    _run_and_compare(f"ragged N=1000 d={d}", t, 0.1, causal, dev, heads=[(0, 0), (1, 2)])
+    t.block_mask = None
+    _run_and_compare(f"ragged dense N=1000 d={d}", t, 0.1, causal, dev, heads=[(0, 1), (1, 0)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_dead_rows(dev, dtype):
+    """Rows that see no key: O = 0, LSE = -inf, no gradient (a zero mask row; and causal with a
+    mask that only allows later blocks)."""
+    N = 384
+    t = workloads.random_case(1, 2, N, 64, dtype, seed=400)
+    t.block_mask = np.array([[1, 0, 0], [0, 0, 0], [1, 1, 1]], dtype=np.uint8)
+    res = _run_and_compare(f"dead rows {dtype}", t, 0.125, False, dev, heads=[(0, 0), (0, 1)])
+    o = G.host_f64(res["o"])
+    assert np.all(o[:, :, 128:256] == 0)
+    assert np.all(np.isneginf(res["lse"][:, :, 128:256].cpu().numpy()))
+    assert np.all(G.host_f64(res["dq"])[:, :, 128:256] == 0)
+    t.block_mask = np.array([[0, 1, 1], [1, 0, 1], [1, 1, 1]], dtype=np.uint8)
+    res = _run_and_compare(f"dead rows causal {dtype}", t, 0.125, True, dev, heads=[(0, 0), (0, 1)])
+    assert np.all(np.isneginf(res["lse"][:, :, 0:128].cpu().numpy()))
+
+
+def test_invariants_on_device_outputs(dev):
+    """Second witnesses on the device results: identical keys give the mean of the visible V;
+    causal row 0 returns V[0] exactly; sums of dV and dK over keys."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    N, d = 256, 64
+    t = workloads.random_case(1, 1, N, d, "bf16", seed=500)
+    t.k[:] = t.k[:, :, :1, :]
+    q = G.to_dev(t.q, "bf16", dev)
+    k = G.to_dev(t.k, "bf16", dev)
+    v = G.to_dev(t.v, "bf16", dev)
+    do = G.to_dev(t.do, "bf16", dev)
+    for causal in (False, True):
+        o, lse = fa.fwd(q, k, v, 0.125, causal)
+        vv = G.host_f64(v)[0, 0]
+        ref = np.cumsum(vv, 0) / np.arange(1, N + 1)[:, None] if causal else np.tile(vv.mean(0), (N, 1))
+        G.check(f"identical keys causal={causal}", G.host_f64(o)[0, 0], ref, G.TOL_BF16, True)
+        if causal:
+            assert np.array_equal(G.host_f64(o)[0, 0, 0], vv[0]), "causal row 0 must return V[0]"
+        dq, dk, dv = fa.bwd(q, k, v, o, lse, do, 0.125, causal)
+        torch.cuda.synchronize()
+        dvs, dos = G.host_f64(dv)[0, 0].sum(0), G.host_f64(do)[0, 0].sum(0)
+        assert np.abs(dvs - dos).max() < 0.05 * math.sqrt(N), "sum_j dV_j = sum_i dO_i"
+        assert np.abs(G.host_f64(dk)[0, 0].sum(0)).max() < 0.05 * math.sqrt(N), "sum_j dK_j = 0"
+
+
+def test_bitwise_reproducible(dev):
+    import torch
+
+    t = workloads.random_case(2, 4, 700, 128, "bf16", seed=600)
+    a = G.run_lib(t, 0.09, True, dev)
+    b = G.run_lib(t, 0.09, True, dev)
+    for kname in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[kname], b[kname]), kname
+
+
+def test_non_default_stream(dev):
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(1, 2, 300, 64, "bf16", seed=700)
+    q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+    ref_o, ref_l = fa.fwd(q, k, v, 0.125, True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = fa.fwd(q, k, v, 0.125, True)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_invalid_call_leaves_outputs_untouched(dev):
+    import ctypes
+
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    q = torch.randn(1, 1, 128, 64, device=dev).to(torch.bfloat16)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((1, 1, 128), 3.0, device=dev)
+    L = fa.lib()
+    p = lambda x: ctypes.c_void_p(x.data_ptr())
+    st = L.flash_attn_fwd(p(q), p(q), p(q), p(o), p(lse), 1, 1, 128, 96, 0.125, 0, None, None)
+    assert st == fa.FA_ERR_HEADDIM
+    st = L.flash_attn_fwd(p(q), p(q), p(q), p(o), p(lse), 1, 1, 128, 64, float("nan"), 0, None, None)
+    assert st == fa.FA_ERR_SCALE
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0) and torch.all(lse == 3.0)
+    with pytest.raises(fa.FlashAttnError):
+        fa.fwd(q, q, q, scale=-1.0)
+
+
+def test_backward_stages_equal_bwd(dev):
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(2, 3, 777, 128, "bf16", seed=800, mask_density=0.5, mask_seed=801)
+    np.fill_diagonal(t.block_mask, 1)
+    q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+    mask = torch.from_numpy(t.block_mask).to(dev)
+    for causal, bm in ((False, None), (True, None), (True, mask)):
+        o, lse = fa.fwd(q, k, v, 0.1, causal, bm)
+        dq, dk, dv = fa.bwd(q, k, v, o, lse, do, 0.1, causal, bm)
+        delta = fa.bwd_preprocess(o, do)
+        dk2, dv2 = fa.bwd_dkdv(q, k, v, do, lse, delta, 0.1, causal, bm)
+        dq2 = fa.bwd_dq(q, k, v, do, lse, delta, 0.1, causal, bm)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
