@@ -33,6 +33,7 @@ int check_common(int B, int H, int N, int d, float scale, int causal, const uint
   const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   if (block_mask && bf16 && nb > FA_MAX_MASK_BLOCKS) return FA_ERR_SHAPE;
   if (!bf16 && bh > 65535) return FA_ERR_SHAPE;  // the fp32 kernels put B*H on grid.y
+  if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_SHAPE;  // one head's slice, as a 31-bit byte range
   const long long tiles = bh * ((N + 127) / 128);
   if (tiles > 0x7fffffffLL) return FA_ERR_SHAPE;
   *elems = e;

@@ -10,16 +10,18 @@
 // Three kernels on one stream:
 //  1. bwd_delta:  D per row (bandwidth-bound, 16-byte loads, shuffle reduction).
 //  2. bwd_dkdv:   one workgroup per (b*h, 128-key block): 4 waves x 32 keys.  K and V of the
-//                 wave's keys stay in registers as MFMA B operands; Q, dO, LSE, D tiles of 64
-//                 rows stream through double-buffered LDS.  S = Q K^T puts one key per lane and
-//                 16 queries in registers, which is the A-operand shape of dV = P^T dO and
-//                 dK = dS^T Q; their B operands (dO and Q with queries as the contraction index)
-//                 come from the same LDS tiles through transposed reads.
-//  3. bwd_dq:     one workgroup per (b*h, 128-query block), K/V tiles double-buffered in LDS:
-//                 S^T = K Q^T and dP^T = V dO^T give one query per lane (the B-operand shape of
-//                 dQ^T = K^T dS^T); K^T is read transposed from the K tile.
+//                 wave's keys stay in registers as MFMA B operands; Q and dO tiles of 64 rows are
+//                 copied global -> LDS asynchronously (double-buffered), LSE and D beside them.
+//                 S = Q K^T puts one key per lane and 16 queries in registers, the A-operand
+//                 shape of dV = P^T dO and dK = dS^T Q; their B operands (dO and Q with queries as
+//                 the contraction index) are read from the same tiles with transposing reads.
+//  3. bwd_dq:     one workgroup per (b*h, 128-query block), K and V tiles of 64 keys copied
+//                 asynchronously into LDS: S^T = K Q^T and dP^T = V dO^T give one query per lane
+//                 (the B-operand shape of dQ^T = K^T dS^T); K^T is read transposed from the K tile.
 // dQ is produced without atomics, so every output element is written once and results are
 // bitwise reproducible run to run.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -55,14 +57,14 @@ template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   constexpr int BKV = 128, BQ = 64;
   constexpr int DC = D / 16, DB = D / 32;
-  constexpr int TILE_BYTES = BQ * D * 2;
-  constexpr int CH = TILE_BYTES / 16 / 256;
-  constexpr int CPR = D / 8;
+  using QT = DmaTile<BQ, D>;  // Q or dO rows (read row-wise and transposed)
 
-  __shared__ __attribute__((aligned(16))) char lds_q[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_do[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float lds_l[2][BQ];
-  __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];
+  __shared__ __attribute__((aligned(1024))) char qbuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(16))) float lbuf[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];
   __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int bcount;
 
@@ -74,8 +76,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   const int k0w = k0 + 32 * w;
   const size_t base = (size_t)bh * N * D;
   const size_t rbase = (size_t)bh * N;
+  const __bf16* __restrict__ Qh = a.q + base;
+  const __bf16* __restrict__ Oh = a.dout + base;
 
-  // ---- query tiles that see this key block
+  // ---- query tiles (of BQ rows) that see this key block
   const int nqt = (N + BQ - 1) / BQ;
   int q_first = 0, ntiles = nqt;
   if (CAUSAL) {
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     return (q_first + t) * BQ;
   };
 
-  // ---- this lane's key: K and V rows as B operands
+  // ---- this lane's key: K and V rows as B operands (features 16c + 8h ..)
   const int key = k0w + c32;
   bf16x8 kreg[DC], vreg[DC];
 #pragma unroll
@@ -118,22 +122,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   }
   const float sl = a.scale_log2;
 
-  uint4 qpre[CH], dpre[CH];
-  float lpre = 0.f, dlpre = 0.f;
-  auto gload = [&](int q0) {
+  // ---- per-lane LDS addresses
+  // A operands (Q, dO rows): row 32 s + perm32(c32) (32 s added per use), features 16c + 8h ..
+  int raddr[DC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      const int qr = q0 + row;
-      if (qr < N) {
-        qpre[i] = *reinterpret_cast<const uint4*>(a.q + base + (size_t)qr * D + col);
-        dpre[i] = *reinterpret_cast<const uint4*>(a.dout + base + (size_t)qr * D + col);
-      } else {
-        qpre[i] = make_uint4(0, 0, 0, 0);
-        dpre[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  for (int c = 0; c < DC; ++c) raddr[c] = QT::off(perm32(c32), 16 * c + 8 * h);
+  // B operands (dO^T, Q^T: queries as the contraction index), transposed read u of feature
+  // block db: lane j of its 16-lane group addresses query row 8h + 4u + j/4 (+ 32 s + 16 mm)
+  int taddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) taddr[u][db] = QT::off4(8 * h + 4 * u + (j >> 2), 32 * db + 16 * g + 4 * (j & 3));
+  }
+
+  QT qdma, odma;
+  qdma.init(w, lane);
+  odma.init(w, lane);
+  float lpre = 0.f, dlpre = 0.f;
+  auto rowstats_load = [&](int q0) {
     if (tid < BQ) {
       const int qr = q0 + tid;
       // rows past N, or rows that see no key, get +inf so that P = 0
@@ -142,80 +151,95 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
       dlpre = qr < N ? a.delta[rbase + qr] : 0.f;
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(lds_q[buf] + lds_off<D>(row, col)) = qpre[i];
-      *reinterpret_cast<uint4*>(lds_do[buf] + lds_off<D>(row, col)) = dpre[i];
-    }
+  auto rowstats_store = [&](int buf) {
     if (tid < BQ) {
-      lds_l[buf][tid] = lpre;
-      lds_d[buf][tid] = dlpre;
+      lbuf[buf][tid] = lpre;
+      dbuf[buf][tid] = dlpre;
     }
   };
 
   if (ntiles > 0) {
-    gload(tile_start(0));
-    lstore(0);
+    const int q0 = tile_start(0);
+    qdma.issue(Qh, N, qbuf0, q0, w);
+    odma.issue(Oh, N, obuf0, q0, w);
+    rowstats_load(q0);
+    rowstats_store(0);
   }
+  wait_dma();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  auto step = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;
+    const char* tq = par ? qbuf1 : qbuf0;
+    const char* to = par ? obuf1 : obuf0;
     const int q0 = tile_start(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) gload(tile_start(t + 1));
-    const char* tq = lds_q[buf];
-    const char* tdo = lds_do[buf];
-
+    if (has_next) {
+      const int qn = tile_start(t + 1);
+      qdma.issue(Qh, N, par ? qbuf0 : qbuf1, qn, w);
+      odma.issue(Oh, N, par ? obuf0 : obuf1, qn, w);
+      rowstats_load(qn);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int qs = q0 + 32 * s;
       if (qs >= N) continue;
       if (CAUSAL && qs + 31 < k0w) continue;  // every query of this step precedes every key of the wave
+      // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`
       f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        sacc = mfma32(lds_row8<D>(tq, 32 * s + c32, 16 * c + 8 * h), kreg[c], sacc);
-        pacc = mfma32(lds_row8<D>(tdo, 32 * s + c32, 16 * c + 8 * h), vreg[c], pacc);
+        sacc = mfma32(lds_b128(tq + raddr[c] + 32 * s * D * 2), kreg[c], sacc);
+        pacc = mfma32(lds_b128(to + raddr[c] + 32 * s * D * 2), vreg[c], pacc);
       }
-      // rows of this lane's accumulators: query 32 s + 8 g + 4 h + e in register 4 g + e
       const bool need_mask = (k0w + 32 > N) || (CAUSAL && qs < k0w + 31);
+      const float* Ls = lbuf[par] + 32 * s;
+      const float* Ds = dbuf[par] + 32 * s;
       bf16x8 pp[2], dsp[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_l[buf][32 * s + 8 * g + 4 * h]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_d[buf][32 * s + 8 * g + 4 * h]);
+      for (int mm = 0; mm < 2; ++mm) {
+        // queries 16 mm + 8 h + 0..7 are consecutive: two float4 reads each for LSE and D
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(Ls + 16 * mm + 8 * h);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(Ls + 16 * mm + 8 * h + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 16 * mm + 8 * h);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 16 * mm + 8 * h + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -l4[e]));
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * mm + e;
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dv = e < 4 ? d0[e] : d1[e - 4];
+          float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
           if (need_mask) {
-            const int qi = qs + 8 * g + 4 * h + e;
+            const int qi = qs + 16 * mm + 8 * h + e;
             if (key >= N || (CAUSAL && key > qi)) p = 0.f;
           }
-          const float ds = p * (pacc[r] - d4[e]);
-          pp[r >> 3][r & 7] = (__bf16)p;
-          dsp[r >> 3][r & 7] = (__bf16)ds;
+          pp[mm][e] = (__bf16)p;
+          dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
         }
       }
-      // dV += P^T dO ; dK += dS^T Q   (contraction over the 32 queries, two chunks of 16)
+      // dV += P^T dO ; dK += dS^T Q  (contraction over the 32 queries, two chunks of 16)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          dvacc[db] = mfma32(pp[mm], lds_tr_operand<D>(tdo, 32 * s + 16 * mm, 32 * db, lane), dvacc[db]);
-          dkacc[db] = mfma32(dsp[mm], lds_tr_operand<D>(tq, 32 * s + 16 * mm, 32 * db, lane), dkacc[db]);
+          const int roff = (32 * s + 16 * mm) * D * 2;
+          dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
+                             dvacc[db]);
+          dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
+                             dkacc[db]);
         }
     }
-
-    if (has_next) lstore(buf ^ 1);
+    if (has_next) rowstats_store(par ^ 1);
+    wait_dma();
     __syncthreads();
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue: lane holds dims 32 db + c32 of keys k0w + 8 g + 4 h + e
+  // ---- epilogue: lane holds feature 32 db + c32 of keys k0w + 8 g + 4 h + e (register 4 g + e)
   const float scale = a.scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -232,15 +256,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
 
 // ------------------------------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a, Sched sc) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
   constexpr int BR = 128, BC = 64;
   constexpr int DC = D / 16, DB = D / 32;
-  constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int CH = TILE_BYTES / 16 / 256;
-  constexpr int CPR = D / 8;
+  using KT = DmaTile<BC, D>;  // K (read row-wise and transposed) or V (row-wise)
 
-  __shared__ __attribute__((aligned(16))) char lds_k[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[KT::BYTES];
   __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int bcount;
 
@@ -251,6 +275,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a,
   const int q0 = qt * BR;
   const size_t base = (size_t)bh * N * D;
   const size_t rbase = (size_t)bh * N;
+  const __bf16* __restrict__ Kh = a.k + base;
+  const __bf16* __restrict__ Vh = a.v + base;
 
   const int nk = (N + BC - 1) / BC;
   int ntiles = nk;
@@ -294,76 +320,78 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdArgs a,
   for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
   const float sl = a.scale_log2;
 
-  uint4 kpre[CH], vpre[CH];
-  auto gload = [&](int k0) {
+  // per-lane LDS addresses: A operands (K, V rows) and the transposed K^T reads
+  int raddr[DC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      const int kr = k0 + row;
-      if (kr < N) {
-        kpre[i] = *reinterpret_cast<const uint4*>(a.k + base + (size_t)kr * D + col);
-        vpre[i] = *reinterpret_cast<const uint4*>(a.v + base + (size_t)kr * D + col);
-      } else {
-        kpre[i] = make_uint4(0, 0, 0, 0);
-        vpre[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int c = 0; c < DC; ++c) raddr[c] = KT::off(perm32(c32), 16 * c + 8 * h);
+  int taddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(lds_k[buf] + lds_off<D>(row, col)) = kpre[i];
-      *reinterpret_cast<uint4*>(lds_v[buf] + lds_off<D>(row, col)) = vpre[i];
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(tile_start(0));
-    lstore(0);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) taddr[u][db] = KT::off4(8 * h + 4 * u + (j >> 2), 32 * db + 16 * g + 4 * (j & 3));
   }
+
+  KT kdma, vdma;
+  kdma.init(w, lane);
+  vdma.init(w, lane);
+  if (ntiles > 0) {
+    kdma.issue(Kh, N, kbuf0, tile_start(0), w);
+    vdma.issue(Vh, N, vbuf0, tile_start(0), w);
+  }
+  wait_dma();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  auto step = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;
+    const char* tk = par ? kbuf1 : kbuf0;
+    const char* tv = par ? vbuf1 : vbuf0;
     const int k0 = tile_start(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) gload(tile_start(t + 1));
-    const char* tk = lds_k[buf];
-    const char* tv = lds_v[buf];
+    if (has_next) {
+      const int kn = tile_start(t + 1);
+      kdma.issue(Kh, N, par ? kbuf0 : kbuf1, kn, w);
+      vdma.issue(Vh, N, par ? vbuf0 : vbuf1, kn, w);
+    }
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w);
-
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (CAUSAL && k0 + 32 * kb > q0 + 32 * w + 31) continue;  // every key of the block follows every query of the wave
+      if (CAUSAL && k0 + 32 * kb > q0 + 32 * w + 31) continue;  // every key of the block follows every query
+      // S^T = K Q^T, dP^T = V dO^T; register r of half h holds key k0 + 32 kb + acc_row(r, h), query qrow
       f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        sacc = mfma32(lds_row8<D>(tk, 32 * kb + c32, 16 * c + 8 * h), qreg[c], sacc);
-        pacc = mfma32(lds_row8<D>(tv, 32 * kb + c32, 16 * c + 8 * h), doreg[c], pacc);
+        sacc = mfma32(lds_b128(tk + raddr[c] + 32 * kb * D * 2), qreg[c], sacc);
+        pacc = mfma32(lds_b128(tv + raddr[c] + 32 * kb * D * 2), doreg[c], pacc);
       }
       bf16x8 dsp[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lse2));
         if (need_mask) {
-          const int kr = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int kr = k0 + 32 * kb + acc_row(r, h);
           if (kr >= N || (CAUSAL && kr > qrow)) p = 0.f;
         }
         dsp[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dval));
       }
-      // dQ^T += K^T dS^T (contraction over the 32 keys of the block)
+      // dQ^T += K^T dS^T (contraction over the 32 keys; dsp[m2] holds keys 16 m2 + 8h + 0..7)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
-          dqacc[db] = mfma32(lds_tr_operand<D>(tk, 32 * kb + 16 * m2, 32 * db, lane), dsp[m2], dqacc[db]);
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int roff = (32 * kb + 16 * m2) * D * 2;
+          dqacc[db] = mfma32(join8(lds_tr4(tk + roff + taddr[0][db]), lds_tr4(tk + roff + taddr[1][db])), dsp[m2],
+                             dqacc[db]);
+        }
     }
-
-    if (has_next) lstore(buf ^ 1);
+    wait_dma();
     __syncthreads();
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (qrow < N) {

@@ -44,53 +44,183 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 // ---------------------------------------------------------------------------------------------
-// LDS tiles: rows of D bf16 (D * 2 bytes, a multiple of 128 bytes), with the 16-byte chunk index
-// inside a row XOR-swizzled by f(row) = 2 (row % 4) + (row / 4) % 2.
-//  * 16-byte row reads (ds_read_b128, 8 lanes per LDS cycle reading 8 consecutive rows at the
-//    same column) hit 8 distinct chunk slots: f takes 8 distinct values over 8 consecutive rows.
-//  * transposed reads (ds_read_b64_tr_b16: 16 lanes read 4 consecutive rows x 32 bytes) hit
-//    8 distinct slots: f(row) / 2 takes 4 distinct values over 4 consecutive rows.
-//  * 16-byte writes of 8 consecutive chunks of one row are a permutation of that row's slots.
+// LDS tiles.  Every MFMA operand is fetched with 16-byte ds_read_b128 (LDS serves these 16 lanes
+// per pass over a 256-byte bank window; the 8-byte transposing read ds_read_b64_tr_b16 moves
+// data at about a quarter of that rate on gfx950, so operands that need the contraction index
+// inside a lane are written transposed into their own tile when the tile is staged instead).
+//
+// A Tile<ROWS, COLS> holds ROWS rows of COLS bf16 with a row stride of COLS*2 + 16 bytes.  The
+// extra 16 bytes shift consecutive rows by one 16-byte bank slot (mod 256 bytes), so 16 lanes
+// reading the same column of 16 different rows of a 32-row group hit 16 distinct slots; and every
+// address is a per-lane base plus a compile-time offset.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int ROWS, int COLS>
+struct Tile {
+  static constexpr int STRIDE = COLS * 2 + 16;
+  static constexpr int BYTES = ROWS * STRIDE;
+  __device__ static constexpr int off(int r, int c) { return r * STRIDE + c * 2; }
+};
 
-// byte offset of element (row, col) in a tile with D columns; col must be a multiple of 4
-template <int D>
-__device__ __forceinline__ int lds_off(int row, int col) {
-  return row * (D * 2) + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
-}
+__device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row, int col) {
-  return *reinterpret_cast<const bf16x8*>(tile + lds_off<D>(row, col));
-}
-
-// Transposed read: returns, for lane l (16-lane group g = l / 16, i = l % 16), the 4 values
-// tile[row_t][col0 + i] for t = 0..3, where lane j of the group addresses tile[row_{j/4}][col0 + 4 (j%4)].
-// Each lane passes its own address; the hardware exchanges the 16-bit elements within the group.
+// Transposing 8-byte LDS read: within each 16-lane group, lane i receives element i % 4 of the
+// 8 bytes addressed by lanes 4t + i / 4 (t = 0..3), i.e. a 4 x 4 block transpose per 4 lanes.
 __device__ __forceinline__ s16x4 lds_tr4(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
-
 __device__ __forceinline__ bf16x8 join8(s16x4 a, s16x4 b) {
   s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// A operand (rows = 32 columns of a row-major LDS tile, k slots = 8 tile rows) read transposed:
-// lane l (half h, c = l % 32) receives tile[row(h, e)][col_base + c] for e = 0..7 with
-// row(h, 4u + t) = row_base + 8u + 4h + t.  This matches the k-slot order of an MFMA C
-// accumulator whose rows 16m + 8u + 4h + t sit in registers 8m + 4u + t.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_tr_operand(const char* tile, int row_base, int col_base, int lane) {
-  const int h = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
-  const int col = col_base + 16 * g + 4 * (j & 3);
-  const int r0 = row_base + 4 * h + (j >> 2);
-  s16x4 lo = lds_tr4(tile + lds_off<D>(r0, col));
-  s16x4 hi = lds_tr4(tile + lds_off<D>(r0 + 8, col));
-  return join8(lo, hi);
+// Row order used for A operands whose MFMA result feeds a later contraction: reading row
+// perm32(i) of a 32-row block into A-row i swaps bits 2 and 3 of the row index.  The C
+// accumulator then holds, in registers 8m .. 8m+7 of lane half h, rows 16m + 8h + 0..7 of the
+// block (consecutive), which is exactly one 8-element k-slot group of a 32x32x16 operand.
+__device__ __forceinline__ constexpr int perm32(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
+// block row held by accumulator register r of lane half h after that permutation
+__device__ __forceinline__ constexpr int acc_row(int r, int h) {
+  return 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1) + (r & 3);
+}
+
+// Global reads through buffer resources: the hardware range check returns zero for any byte
+// offset at or past num_records, which covers the ragged last tile of a head without branches.
+// A resource spans one head's [N, d] slice (at most 2^31 - 1 bytes, checked on the host).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit data, no format conversion
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
+}
+__device__ __forceinline__ uint4 load16(const Rsrc& r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint2 load8(const Rsrc& r, int byte_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds): no registers, no VALU.  One
+// instruction moves 64 lanes x 16 bytes into 1 KB of LDS, lane i landing at base + 16 i; the
+// global address of each lane is free, so a tile lands in whatever 16-byte-chunk order the
+// reads want.  The issuing wave waits for its copies with vmcnt(0); a barrier then publishes
+// the tile to the other waves.
+//
+// DmaTile<R, D, SW> stages R rows x D bf16 (R*D/8 16-byte chunks, a multiple of 256) with the
+// chunk order "physical chunk = logical chunk ^ SW(row)".
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+__device__ __forceinline__ void dma16(const Rsrc& r, void* lds_block, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds_block, 16, voff, soff, 0, 0);
+}  // soff stays 0 in this library: the range check does not cover it
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte chunk swizzle (row = tile row, D = row length in bf16), good for both read patterns:
+//  row reads: 16 lanes read the same logical chunk of 16 consecutive rows -> 16 distinct slots
+//             of the 256-byte bank window (d = 128: one row per window, f is a bijection on
+//             row bits 0-3; d = 64: two rows per window, f is a bijection on row bits 1-3);
+//  transposed reads: 16 lanes read 2 adjacent chunks of 4 consecutive rows -> the 4 chunk pairs
+//             land on distinct pairs of slots (f >> 1 differs across the rows sharing a window).
+template <int D>
+__device__ __forceinline__ constexpr int sw_dual(int row) {
+  return D >= 128 ? (2 * (row & 3) + ((row >> 2) & 1) + 8 * ((row >> 3) & 1))
+                  : (2 * ((row >> 1) & 1) + 4 * ((row >> 2) & 1) + ((row >> 3) & 1));
+}
+
+template <int R, int D>
+struct DmaTile {
+  static constexpr int CPR = D / 8;
+  static constexpr int BYTES = R * D * 2;
+  static constexpr int CH = R * CPR / 256;  // instructions per wave (4 waves)
+  static_assert(CH >= 1 && (R * CPR) % 256 == 0, "tile too small for 4 waves");
+  __device__ static constexpr int sw(int row) { return sw_dual<D>(row); }
+  // byte offset in the tile of the 16-byte chunk holding (row, col), col a multiple of 8
+  __device__ static constexpr int off(int row, int col) { return row * D * 2 + (((col >> 3) ^ sw(row)) << 4); }
+  // byte offset of (row, col) for a transposed 8-byte read, col a multiple of 4
+  __device__ static constexpr int off4(int row, int col) { return off(row, col) + (col & 7) * 2; }
+  int voff[CH];  // per-lane global byte offsets relative to the tile's first row
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = 64 * (CH * w + i) + lane;
+      const int row = slot / CPR, pchunk = slot % CPR;
+      voff[i] = (row * D + ((pchunk ^ sw(row)) << 3)) * 2;
+    }
+  }
+  // enqueue the copy of rows [row0, row0 + R) of `head` (N rows) into `tile`; rows >= N read
+  // as zero.  The resource starts at row0 and spans only rows row0 .. N-1, so the hardware
+  // range check (which covers the per-lane offset) does the clipping.
+  __device__ __forceinline__ void issue(const __bf16* head, int N, char* tile, int row0, int w) const {
+    const Rsrc r = make_rsrc(head + (size_t)row0 * D, max(N - row0, 0) * D * 2);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(r, tile + 1024 * (CH * w + i), voff[i], 0);
+  }
+};
+
+// Row-major staging of R rows x D columns (rows >= N read as zero): 16-byte global loads into
+// registers, then 16-byte LDS stores.  Split in two so the loads for the next tile can be in
+// flight while the current tile is being used.
+template <int R, int D>
+struct RowStage {
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int CH = R * D / 8 / 256;    // chunks per thread
+  static_assert(CH >= 1 && (R * D / 8) % 256 == 0, "tile too small for 256 threads");
+  uint4 reg[CH];
+  __device__ __forceinline__ void load(const Rsrc& src, int row0, int tid) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      reg[i] = load16(src, ((row0 + row) * D + col) * 2);
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / CPR, col = (cidx % CPR) * 8;
+      *reinterpret_cast<uint4*>(tile + Tile<R, D>::off(row, col)) = reg[i];
+    }
+  }
+};
+
+// Transposed staging: R rows x D columns of global memory land as Tile<D, R> (column c of the
+// source becomes LDS row c).  Each of the first (R/8)*(D/4) threads moves one 8-row x 4-column
+// block: eight 8-byte loads, a 16-bit transpose in registers, four 16-byte LDS stores.
+template <int R, int D>
+struct TransStage {
+  static constexpr int RG = R / 8;            // row groups
+  static constexpr int NB = RG * (D / 4);     // blocks
+  static_assert(NB <= 256, "one block per thread");
+  uint2 reg[8];
+  __device__ __forceinline__ void load(const Rsrc& src, int row0, int tid) {
+    if (tid < NB) {
+      const int rg = tid % RG, cg = tid / RG;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) reg[e] = load8(src, ((row0 + 8 * rg + e) * D + 4 * cg) * 2);
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+    if (tid < NB) {
+      const int rg = tid % RG, cg = tid / RG;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 o;
+        unsigned* ow = reinterpret_cast<unsigned*>(&o);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const unsigned x = (c < 2) ? reg[2 * wd].x : reg[2 * wd].y;
+          const unsigned y = (c < 2) ? reg[2 * wd + 1].x : reg[2 * wd + 1].y;
+          ow[wd] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        }
+        *reinterpret_cast<uint4*>(tile + Tile<D, R>::off(4 * cg + c, 8 * rg)) = o;
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 // wave64 cross-half reductions: lanes l and l ^ 32 hold partial results for the same query.

@@ -11,17 +11,23 @@
 //
 // gfx950 mapping
 //  * workgroup = 4 waves x 32 query rows (BR = 128 rows, one mask block), K/V tiles of BC = 64
-//    keys double-buffered in LDS (global loads for tile t+1 are issued before the math of tile t
-//    and written to the other buffer after it; one barrier per tile).
+//    keys copied global -> LDS asynchronously (buffer_load ... lds: no registers, no VALU) and
+//    software-pipelined: while the exponentials of tile t run on the VALU, the MFMAs already
+//    compute the scores of tile t+1, so K is copied two tiles ahead and V one tile ahead (each
+//    double-buffered; one barrier per tile).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: Q^T is the B operand, held in registers for the
 //    whole kernel; K rows are the A operand (16-byte LDS reads).  Each lane then holds one query
 //    (lane % 32) and 16 keys per 32-key block, so the row max and row sum are in-lane plus one
 //    v_permlane32_swap between the two wave halves.
 //  * O^T += V^T P^T: P^T (bf16, from the S^T registers) is the B operand as is; V^T is read
-//    transposed from the row-major V tile with ds_read_b64_tr_b16.
+//    from the row-major V tile with the transposing ds_read_b64_tr_b16.  K rows are read in a
+//    bit-permuted order that makes each lane's 8 P values 8 consecutive keys.  Both tiles use
+//    a 16-byte-chunk XOR swizzle that keeps their reads free of LDS bank conflicts.
 //  * exponentials in base 2 with scale*log2(e) folded into one FMA; the running maximum is only
 //    moved when a new score exceeds it by more than 2^8, so most tiles skip the O rescale (the
 //    result is the same: numerator and denominator always share the offset).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -34,14 +40,15 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   constexpr int BR = 128, BC = 64;
-  constexpr int DC = D / 16;                // 16-wide contraction chunks over d
-  constexpr int DB = D / 32;                // 32-row output blocks over d
-  constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int CH = TILE_BYTES / 16 / 256;  // 16-byte chunks per thread per tile
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int DC = D / 16;  // 16-wide contraction chunks over d
+  constexpr int DB = D / 32;  // 32-row output blocks over d
+  using KT = DmaTile<BC, D>;  // K rows, read 16 bytes per lane
+  using VT = DmaTile<BC, D>;  // V rows, read transposed (ds_read_b64_tr_b16)
 
-  __shared__ __attribute__((aligned(16))) char lds_k[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[VT::BYTES];
   __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int bcount;
 
@@ -57,9 +64,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
 
   // ---- key tiles this query block visits
   const int nk = (N + BC - 1) / BC;
-  int kv_end = nk;
-  if (CAUSAL) kv_end = min(nk, (min(q0 + BR, N) - 1) / BC + 1);
-  int ntiles = kv_end;
+  int ntiles = nk;
+  if (CAUSAL) ntiles = min(nk, (min(q0 + BR, N) - 1) / BC + 1);
   if (SPARSE) {
     const int qb = q0 / kMaskBlock;
     const int hi = CAUSAL ? qb + 1 : a.nb;
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     return t * BC;
   };
 
-  // ---- Q^T operand in registers
+  // ---- Q^T operand in registers (B operand: lane holds query q0 + 32w + c32, features 16c + 8h ..)
   const int qrow = q0 + 32 * w + c32;
   bf16x8 qreg[DC];
 #pragma unroll
@@ -91,55 +97,65 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   float lsum = 0.f;          // this lane's partial sum of exponentials
   const float sl = a.scale_log2;
 
-  // ---- global -> registers -> LDS staging of one K/V tile
-  uint4 kpre[CH], vpre[CH];
-  auto gload = [&](int k0) {
+  // ---- per-lane LDS addresses (the chunk swizzle of each tile depends only on the lane)
+  // K operand: row 32 kb + perm32(c32), features 16c + 8h .. (one 16-byte chunk)
+  int kaddr[DC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      const int key = k0 + row;
-      if (key < N) {
-        kpre[i] = *reinterpret_cast<const uint4*>(K + (size_t)key * D + col);
-        vpre[i] = *reinterpret_cast<const uint4*>(V + (size_t)key * D + col);
-      } else {
-        kpre[i] = make_uint4(0, 0, 0, 0);
-        vpre[i] = make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < DC; ++c) kaddr[c] = KT::off(perm32(c32), 16 * c + 8 * h);
+  // V^T operand, transposed read u (u = 0, 1) of feature block db: lane j of its 16-lane group
+  // addresses key row 16m + 8h + 4u + j/4 (16m added per use), features 32db + 16g + 4(j%4) ..
+  int vaddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 8 * h + 4 * u + (j >> 2), col = 32 * db + 16 * g + 4 * (j & 3);
+        vaddr[u][db] = VT::off4(row, col);
       }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(lds_k[buf] + lds_off<D>(row, col)) = kpre[i];
-      *reinterpret_cast<uint4*>(lds_v[buf] + lds_off<D>(row, col)) = vpre[i];
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(tile_start(0));
-    lstore(0);
   }
-  __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int k0 = tile_start(t);
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) gload(tile_start(t + 1));
-    const char* tk = lds_k[buf];
-    const char* tv = lds_v[buf];
+  KT kdma;
+  VT vdma;
+  kdma.init(w, lane);
+  vdma.init(w, lane);
 
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+  // S^T = K Q^T for two 32-key blocks; register r of half h holds key k0 + 32 kb + acc_row(r, h)
+  auto scores = [&](const char* tk, f32x16(&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero16();
 #pragma unroll
-      for (int c = 0; c < DC; ++c) s[kb] = mfma32(lds_row8<D>(tk, kb * 32 + c32, 16 * c + 8 * h), qreg[c], s[kb]);
+      for (int c = 0; c < DC; ++c) s[kb] = mfma32(lds_b128(tk + kaddr[c] + 32 * kb * D * 2), qreg[c], s[kb]);
     }
+  };
+
+  // Software pipeline over key tiles (K runs one tile ahead of V):
+  //   iteration t:  copies of K[t+2], V[t+1] in flight;  softmax of S[t] next to the MFMAs of
+  //                 S[t+1] = K[t+1] Q^T;  O += V[t] P[t];  wait for the copies; barrier.
+  // K tiles alternate between kbuf0/kbuf1 and V tiles between vbuf0/vbuf1, so the buffer a copy
+  // lands in during iteration t is never one read in iteration t.
+  f32x16 s_cur[2];
+  if (ntiles > 0) {
+    kdma.issue(K, N, kbuf0, tile_start(0), w);
+    vdma.issue(V, N, vbuf0, tile_start(0), w);
+    if (ntiles > 1) kdma.issue(K, N, kbuf1, tile_start(1), w);
+  }
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 0) scores(kbuf0, s_cur);
+
+  auto step = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;  // t % 2
+    char* const k_next = par ? kbuf0 : kbuf1;      // holds K[t+1]
+    char* const k_free = par ? kbuf1 : kbuf0;      // held K[t]; receives K[t+2]
+    char* const v_cur = par ? vbuf1 : vbuf0;       // holds V[t]
+    char* const v_free = par ? vbuf0 : vbuf1;      // held V[t-1]; receives V[t+1]
+    const int k0 = tile_start(t);
+    const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles;
+    if (has2) kdma.issue(K, N, k_free, tile_start(t + 2), w);
+    if (has1) vdma.issue(V, N, v_free, tile_start(t + 1), w);
 
     // element masks: the causal diagonal and the key tail
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w);
@@ -148,17 +164,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
+          const int key = k0 + 32 * kb + acc_row(r, h);
+          if (key >= N || (CAUSAL && key > qrow)) s_cur[kb][r] = neg_inf();
         }
     }
 
-    // online softmax
-    float mt = s[0][0];
+    // online softmax: running max moves only when a score exceeds it by more than 2^8
+    float mt = s_cur[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_cur[kb][r]);
     mt = half_swap_max(mt) * sl;
     const float m_new = (mt > m_used + kRescaleThreshold) ? mt : m_used;
     const float alpha = (m_new == m_used) ? 1.f : fast_exp2(m_used - m_new);
@@ -170,32 +186,49 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     }
     const float msub = (m_used == neg_inf()) ? 0.f : m_used;
 
-    // P in fp32 feeds the row sum (so LSE carries fp32 error only); its bf16 rounding feeds PV
+    // next tile's scores: independent of the exponentials below, so the two can overlap
+    f32x16 s_nxt[2];
+    if (has1) scores(k_next, s_nxt);
+
+    // P in fp32 feeds the row sum (so LSE carries fp32 error only); its bf16 rounding feeds PV.
+    // pk[2 kb + m2] holds keys k0 + 32 kb + 16 m2 + 8h + 0..7: one k-slot group of the PV MFMA.
     bf16x8 pk[4];
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(__builtin_fmaf(s[kb][8 * u + e], sl, -msub));
+          const float pv = fast_exp2(__builtin_fmaf(s_cur[kb][8 * m2 + e], sl, -msub));
           part[e & 3] += pv;
-          pk[2 * kb + u][e] = (__bf16)pv;
+          pk[2 * kb + m2][e] = (__bf16)pv;
         }
     lsum += (part[0] + part[1]) + (part[2] + part[3]);
 
-    // O^T += V^T P^T over the 64 keys (4 contraction chunks of 16)
+    // O^T += V^T P^T over the 64 keys (4 contraction chunks of 16; V^T read transposed)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) oacc[db] = mfma32(lds_tr_operand<D>(tv, 16 * m, 32 * db, lane), pk[m], oacc[db]);
+      for (int m = 0; m < 4; ++m) {
+        const char* vb = v_cur + 16 * m * D * 2;
+        oacc[db] = mfma32(join8(lds_tr4(vb + vaddr[0][db]), lds_tr4(vb + vaddr[1][db])), pk[m], oacc[db]);
+      }
 
-    if (has_next) lstore(buf ^ 1);
+    wait_dma();
     __syncthreads();
+    if (has1) {
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+    }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue
+  // ---- epilogue: lane holds features 32 db + 8 g + 4 h + e of query qrow in register 4 g + e
   const float ltot = half_swap_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (qrow < N) {
