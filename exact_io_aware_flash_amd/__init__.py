@@ -56,11 +56,11 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_bwd.restype = i
     L.flash_attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp, vp]
     L.flash_attn_bwd_f32.restype = i
-    L.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
     L.flash_attn_bwd_preprocess.restype = i
-    L.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_bwd_dkdv.restype = i
-    L.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_bwd_dq.restype = i
     L.flash_attn_status_string.argtypes = [i]
     L.flash_attn_status_string.restype = ctypes.c_char_p
@@ -178,23 +178,36 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, b
 
 
 # ---------------------------------------------------------------------------------------------
-# The three backward stages one by one (bf16).  Enqueued in this order they equal bwd().
-def bwd_preprocess(o, do, delta=None, stream=None):
-    """delta[b, h, i] = sum_c do * o (float32 [B, H, N])."""
+# The three backward stages one by one (bf16).  Enqueued in this order with one workspace they
+# equal bwd().
+def new_workspace(B: int, H: int, N: int, d: int, device):
+    """A workspace tensor of flash_attn_bwd_workspace_bytes() bytes (torch allocations are
+    256-byte aligned)."""
+    import torch
+
+    return torch.empty(workspace_bytes(B, H, N, d), dtype=torch.uint8, device=device)
+
+
+def _ws_bytes(ws):
+    return ws.numel() * ws.element_size()
+
+
+def bwd_preprocess(q, o, do, workspace=None, stream=None):
+    """Pre-pass: D = rowsum(dO * O) into `workspace`."""
     import torch
 
     B, H, N, d = o.shape
-    _check(o, "o", torch.bfloat16, (B, H, N, d), o.device)
-    _check(do, "do", torch.bfloat16, (B, H, N, d), o.device)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
-    _check(delta, "delta", torch.float32, (B, H, N), o.device)
-    st = lib().flash_attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _stream(stream))
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), o.device)
+    workspace = new_workspace(B, H, N, d, o.device) if workspace is None else workspace
+    st = lib().flash_attn_bwd_preprocess(_ptr(q), _ptr(o), _ptr(do), _ptr(workspace), _ws_bytes(workspace), B, H,
+                                         N, d, _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_preprocess")
-    return delta
+    return workspace
 
 
-def bwd_dkdv(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None, dk=None, dv=None, stream=None):
+def bwd_dkdv(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=None, dk=None, dv=None, stream=None):
     import torch
 
     B, H, N, d = q.shape
@@ -202,19 +215,19 @@ def bwd_dkdv(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None,
     for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
         _check(t, name, torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
-    _check(delta, "delta", torch.float32, (B, H, N), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     bm = _mask_arg(block_mask, N, dev)
-    st = lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
-                                   B, H, N, d, scale, int(bool(causal)), _ptr(bm), _stream(stream))
+    st = lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+                                   _ws_bytes(workspace), _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
+                                   _ptr(bm), _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_dkdv")
     return dk, dv
 
 
-def bwd_dq(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None, dq=None, stream=None):
+def bwd_dq(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=None, dq=None, stream=None):
     import torch
 
     B, H, N, d = q.shape
@@ -222,12 +235,12 @@ def bwd_dq(q, k, v, do, lse, delta, scale=None, causal=False, block_mask=None, d
     for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
         _check(t, name, torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
-    _check(delta, "delta", torch.float32, (B, H, N), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     bm = _mask_arg(block_mask, N, dev)
-    st = lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq), B, H, N, d,
-                                 scale, int(bool(causal)), _ptr(bm), _stream(stream))
+    st = lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+                                 _ws_bytes(workspace), _ptr(dq), B, H, N, d, scale, int(bool(causal)), _ptr(bm),
+                                 _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_dq")
     return dq

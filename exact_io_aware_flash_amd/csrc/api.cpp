@@ -58,11 +58,12 @@ int check_alias(const Range* in, int nin, const Range* out, int nout) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-size_t workspace_bytes(int B, int H, int N) {
-  if (B < 1 || H < 1 || N < 1) return 0;
-  const size_t b = (size_t)B * H * N * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+size_t workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return fa::ws_bytes((long long)B * H, N);
 }
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 template <typename T>
 int fwd_checked(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d, float scale,
@@ -85,15 +86,16 @@ int bwd_checked(const T* q, const T* k, const T* v, const T* o, const T* dout, c
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale, causal, block_mask, bf16, elems);
   if (st != FA_OK) return st;
-  if (!ws || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
+  if (!ws || ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (!aligned256(ws)) return FA_ERR_ALIGN;
   const long long tb = *elems * (long long)sizeof(T), lb = (long long)B * H * N * 4;
   const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   Range in[7] = {rng(q, tb),    rng(k, tb),   rng(v, tb), rng(o, tb), rng(dout, tb), rng(lse, lb),
                  rng(block_mask, block_mask ? nb * nb : 0)};
-  Range out[4] = {rng(dq, tb), rng(dk, tb), rng(dv, tb), rng(ws, (long long)workspace_bytes(B, H, N))};
+  Range out[4] = {rng(dq, tb), rng(dk, tb), rng(dv, tb), rng(ws, (long long)workspace_bytes(B, H, N, d))};
   return check_alias(in, 7, out, 4);
 }
 
@@ -122,7 +124,7 @@ int stage_checked(const void* const* in, const long long* in_bytes, int nin, voi
 }
 
 fa::BwdArgs stage_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                       const float* lse, const float* delta, void* dq, void* dk, void* dv, int B, int H, int N,
+                       const float* lse, const void* workspace, void* dq, void* dk, void* dv, int B, int H, int N,
                        int d, float scale, int causal, const uint8_t* block_mask) {
   fa::BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
@@ -134,7 +136,7 @@ fa::BwdArgs stage_args(const void* q, const void* k, const void* v, const void* 
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
-  a.delta = const_cast<float*>(delta);
+  a.delta = static_cast<float*>(const_cast<void*>(workspace));
   a.mask = block_mask;
   a.N = N;
   a.d = d;
@@ -166,10 +168,7 @@ const char* flash_attn_status_string(int status) {
   }
 }
 
-size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d) {
-  (void)d;
-  return workspace_bytes(B, H, N);
-}
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d) { return workspace_bytes(B, H, N, d); }
 
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                    float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
@@ -223,28 +222,12 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes_, int B, int H, int N, int d,
                    float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
   long long elems = 0;
-  fa::BwdArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
-  a.o = static_cast<const __bf16*>(o);
-  a.dout = static_cast<const __bf16*>(dout);
-  a.lse = lse;
-  a.dq = static_cast<__bf16*>(dq);
-  a.dk = static_cast<__bf16*>(dk);
-  a.dv = static_cast<__bf16*>(dv);
-  int st = bwd_checked(a.q, a.k, a.v, a.o, a.dout, lse, a.dq, a.dk, a.dv, workspace, workspace_bytes_, B, H, N, d,
-                       scale, causal, block_mask, true, &elems);
+  int st = bwd_checked(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                       static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse,
+                       static_cast<__bf16*>(dq), static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), workspace,
+                       workspace_bytes_, B, H, N, d, scale, causal, block_mask, true, &elems);
   if (st != FA_OK) return st;
-  a.delta = static_cast<float*>(workspace);
-  a.mask = block_mask;
-  a.N = N;
-  a.d = d;
-  a.BH = B * H;
-  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
-  a.causal = causal;
-  a.scale = scale;
-  a.scale_log2 = scale * fa::kLog2e;
+  const fa::BwdArgs a = stage_args(q, k, v, o, dout, lse, workspace, dq, dk, dv, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_bf16(a, stream));
 }
 
@@ -278,47 +261,53 @@ int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const flo
   return status_of(fa::launch_bwd_f32(a, stream));
 }
 
-int flash_attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N, int d,
-                              hipStream_t stream) {
-  const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
-  const void* in[2] = {o, dout};
-  const long long ib[2] = {tb, tb};
-  void* out[1] = {delta};
-  const long long ob[1] = {rb};
-  int st = stage_checked(in, ib, 2, out, ob, 1, B, H, N, d, 1.0f, 0, nullptr);
+int flash_attn_bwd_preprocess(const void* q, const void* o, const void* dout, void* workspace,
+                              size_t workspace_bytes_, int B, int H, int N, int d, hipStream_t stream) {
+  const long long tb = (long long)B * H * N * d * 2;
+  const void* in[3] = {q, o, dout};
+  const long long ib[3] = {tb, tb, tb};
+  void* out[1] = {workspace};
+  const long long ob[1] = {(long long)workspace_bytes(B, H, N, d)};
+  int st = stage_checked(in, ib, 3, out, ob, 1, B, H, N, d, 1.0f, 0, nullptr);
   if (st != FA_OK) return st;
-  const fa::BwdArgs a = stage_args(nullptr, nullptr, nullptr, o, dout, nullptr, delta, nullptr, nullptr, nullptr,
-                                   B, H, N, d, 1.0f, 0, nullptr);
+  if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return FA_ERR_ALIGN;
+  const fa::BwdArgs a = stage_args(q, nullptr, nullptr, o, dout, nullptr, workspace, nullptr, nullptr, nullptr, B, H,
+                                   N, d, 1.0f, 0, nullptr);
   return status_of(fa::launch_bwd_delta_bf16(a, stream));
 }
 
 int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                        const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                        const uint8_t* block_mask, hipStream_t stream) {
+                        const void* workspace, size_t workspace_bytes_, void* dk, void* dv, int B, int H, int N,
+                        int d, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
   const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
-  const void* in[6] = {q, k, v, dout, lse, delta};
-  const long long ib[6] = {tb, tb, tb, tb, rb, rb};
+  const void* in[6] = {q, k, v, dout, lse, workspace};
+  const long long ib[6] = {tb, tb, tb, tb, rb, (long long)workspace_bytes(B, H, N, d)};
   void* out[2] = {dk, dv};
   const long long ob[2] = {tb, tb};
   int st = stage_checked(in, ib, 6, out, ob, 2, B, H, N, d, scale, causal, block_mask);
   if (st != FA_OK) return st;
+  if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return FA_ERR_ALIGN;
   const fa::BwdArgs a =
-      stage_args(q, k, v, nullptr, dout, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, block_mask);
+      stage_args(q, k, v, nullptr, dout, lse, workspace, nullptr, dk, dv, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_dkdv_bf16(a, stream));
 }
 
 int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                      const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
-                      const uint8_t* block_mask, hipStream_t stream) {
+                      const void* workspace, size_t workspace_bytes_, void* dq, int B, int H, int N, int d,
+                      float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
   const long long tb = (long long)B * H * N * d * 2, rb = (long long)B * H * N * 4;
-  const void* in[6] = {q, k, v, dout, lse, delta};
-  const long long ib[6] = {tb, tb, tb, tb, rb, rb};
+  const void* in[6] = {q, k, v, dout, lse, workspace};
+  const long long ib[6] = {tb, tb, tb, tb, rb, (long long)workspace_bytes(B, H, N, d)};
   void* out[1] = {dq};
   const long long ob[1] = {tb};
   int st = stage_checked(in, ib, 6, out, ob, 1, B, H, N, d, scale, causal, block_mask);
   if (st != FA_OK) return st;
+  if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return FA_ERR_ALIGN;
   const fa::BwdArgs a =
-      stage_args(q, k, v, nullptr, dout, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, block_mask);
+      stage_args(q, k, v, nullptr, dout, lse, workspace, dq, nullptr, nullptr, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_dq_bf16(a, stream));
 }
 

@@ -168,6 +168,70 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   wait_dma();
   __syncthreads();
 
+  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..).  MASK: element masks
+  // for the key tail and the causal diagonal; interior tiles run without them.  Every MFMA
+  // operand is loaded before the MFMAs that use it (the scheduling groups keep the compiler from
+  // sinking the LDS reads next to their uses, where their latency would stall the MFMA pipe).
+  auto half = [&](auto maskc, const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
+    constexpr bool MASK = decltype(maskc)::value;
+    // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`
+    f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      sacc = mfma32(lds_b128(tq + raddr[c] + 32 * s * D * 2), kreg[c], sacc);
+      pacc = mfma32(lds_b128(to + raddr[c] + 32 * s * D * 2), vreg[c], pacc);
+    }
+    // operand reads run two MFMA pairs ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int c = 0; c < DC - 2; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
+    bf16x8 pp[2], dsp[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(Ls + 32 * s + 16 * mm + 8 * h);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(Ls + 32 * s + 16 * mm + 8 * h + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 32 * s + 16 * mm + 8 * h);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 32 * s + 16 * mm + 8 * h + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * mm + e;
+        const float lv = e < 4 ? l0[e] : l1[e - 4];
+        const float dv = e < 4 ? d0[e] : d1[e - 4];
+        float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
+        if (MASK) {
+          const int qi = qs + 16 * mm + 8 * h + e;
+          if (key >= N || (CAUSAL && key > qi)) p = 0.f;
+        }
+        pp[mm][e] = (__bf16)p;
+        dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
+      }
+    }
+    // dV += P^T dO ; dK += dS^T Q (contraction over the 32 queries, two chunks of 16); each MFMA
+    // takes one transposed B operand (two 8-byte transposing reads), kept two MFMAs ahead
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int roff = (32 * s + 16 * mm) * D * 2;
+        dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
+                           dvacc[db]);
+        dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
+                           dkacc[db]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+  };
+
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tq = par ? qbuf1 : qbuf0;
@@ -180,54 +244,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
       odma.issue(Oh, N, par ? obuf0 : obuf1, qn, w);
       rowstats_load(qn);
     }
+    const float* Ls = lbuf[par];
+    const float* Ds = dbuf[par];
+    // tiles touching the causal diagonal or the key tail take the masked path; queries past N
+    // need no mask (their LSE is +inf, so P = 0)
+    // (d = 64 runs one body for every tile: a second copy costs it its second wave per SIMD)
+    const bool tile_mask = (D == 64) || (k0 + BKV > N) || (CAUSAL && q0 < k0 + BKV - 1);
+    if (!tile_mask) {
+      half(std::false_type{}, tq, to, Ls, Ds, 0, q0);
+      half(std::false_type{}, tq, to, Ls, Ds, 1, q0 + 32);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int qs = q0 + 32 * s;
-      if (qs >= N) continue;
-      if (CAUSAL && qs + 31 < k0w) continue;  // every query of this step precedes every key of the wave
-      // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`
-      f32x16 sacc = zero16(), pacc = zero16();
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        sacc = mfma32(lds_b128(tq + raddr[c] + 32 * s * D * 2), kreg[c], sacc);
-        pacc = mfma32(lds_b128(to + raddr[c] + 32 * s * D * 2), vreg[c], pacc);
+      for (int s = 0; s < 2; ++s) {
+        const int qs = q0 + 32 * s;
+        if (qs >= N) continue;
+        if (CAUSAL && qs + 31 < k0w) continue;  // every query of this half precedes every key of the wave
+        half(std::true_type{}, tq, to, Ls, Ds, s, qs);
       }
-      const bool need_mask = (k0w + 32 > N) || (CAUSAL && qs < k0w + 31);
-      const float* Ls = lbuf[par] + 32 * s;
-      const float* Ds = dbuf[par] + 32 * s;
-      bf16x8 pp[2], dsp[2];
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        // queries 16 mm + 8 h + 0..7 are consecutive: two float4 reads each for LSE and D
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(Ls + 16 * mm + 8 * h);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(Ls + 16 * mm + 8 * h + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 16 * mm + 8 * h);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 16 * mm + 8 * h + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * mm + e;
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv = e < 4 ? d0[e] : d1[e - 4];
-          float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
-          if (need_mask) {
-            const int qi = qs + 16 * mm + 8 * h + e;
-            if (key >= N || (CAUSAL && key > qi)) p = 0.f;
-          }
-          pp[mm][e] = (__bf16)p;
-          dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
-        }
-      }
-      // dV += P^T dO ; dK += dS^T Q  (contraction over the 32 queries, two chunks of 16)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int roff = (32 * s + 16 * mm) * D * 2;
-          dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
-                             dvacc[db]);
-          dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
-                             dkacc[db]);
-        }
     }
     if (has_next) rowstats_store(par ^ 1);
     wait_dma();
@@ -365,6 +398,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
         sacc = mfma32(lds_b128(tk + raddr[c] + 32 * kb * D * 2), qreg[c], sacc);
         pacc = mfma32(lds_b128(tv + raddr[c] + 32 * kb * D * 2), doreg[c], pacc);
       }
+      // operand reads run two MFMA pairs ahead of the MFMAs that consume them
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int c = 0; c < DC - 2; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       bf16x8 dsp[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -384,6 +425,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
           dqacc[db] = mfma32(join8(lds_tr4(tk + roff + taddr[0][db]), lds_tr4(tk + roff + taddr[1][db])), dsp[m2],
                              dqacc[db]);
         }
+      // each MFMA takes one transposed operand (two 8-byte transposing reads), kept two ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * DB - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
     }
     wait_dma();
     __syncthreads();

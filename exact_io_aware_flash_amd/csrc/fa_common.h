@@ -160,6 +160,34 @@ struct DmaTile {
   }
 };
 
+// A slab of a feature-major copy: R feature rows x C consecutive positions (columns), the
+// global rows `stride` elements apart.  Same chunk swizzle as DmaTile<., C>; each row is read
+// 16 bytes per lane (16 lanes = 16 consecutive rows at one chunk: distinct bank slots).
+template <int R, int C>
+struct SlabDma {
+  static constexpr int CPR = C / 8;
+  static constexpr int BYTES = R * C * 2;
+  static constexpr int CH = R * CPR / 256;
+  static_assert(CH >= 1 && (R * CPR) % 256 == 0, "slab too small for 4 waves");
+  __device__ static constexpr int off(int row, int col) { return row * C * 2 + (((col >> 3) ^ sw_dual<C>(row)) << 4); }
+  int voff[CH];
+  __device__ __forceinline__ void init(int w, int lane, int stride) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = 64 * (CH * w + i) + lane;
+      const int row = slot / CPR, pchunk = slot % CPR;
+      voff[i] = (row * stride + ((pchunk ^ sw_dual<C>(row)) << 3)) * 2;
+    }
+  }
+  // enqueue columns [col0, col0 + C) of every row of the copy at `head` (R rows of `stride`
+  // elements; col0 + C <= stride) into `tile`
+  __device__ __forceinline__ void issue(const __bf16* head, int stride, char* tile, int col0, int w) const {
+    const Rsrc r = make_rsrc(head + col0, (R * stride - col0) * 2);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(r, tile + 1024 * (CH * w + i), voff[i], 0);
+  }
+};
+
 // Row-major staging of R rows x D columns (rows >= N read as zero): 16-byte global loads into
 // registers, then 16-byte LDS stores.  Split in two so the loads for the next tile can be in
 // flight while the current tile is being used.

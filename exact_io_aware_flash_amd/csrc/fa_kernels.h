@@ -37,6 +37,9 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Backward workspace: delta (float32 [BH, N]), 256-byte aligned size.
+inline size_t ws_bytes(long long BH, int N) { return ((size_t)BH * N * 4 + 255) & ~(size_t)255; }
+
 struct F32Args {
   const float* q;
   const float* k;

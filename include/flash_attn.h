@@ -53,7 +53,7 @@ enum {
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, a size overflows, or nb > FA_MAX_MASK_BLOCKS */
   FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
-  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (the workspace: 256-byte) */
   FA_ERR_SCALE = 5,     /* scale not finite or not > 0 */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than flash_attn_bwd_workspace_bytes() */
   FA_ERR_HIP = 7,       /* a kernel launch failed */
@@ -82,9 +82,9 @@ int flash_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
                        int B, int H, int N, int d, float scale, int causal,
                        const uint8_t *block_mask, hipStream_t stream);
 
-/* Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for this shape (the
- * per-row D = rowsum(dO * O) of the pre-pass, float32 [B, H, N], rounded up to 256 bytes).
- * Returns 0 if B, H or N < 1. */
+/* Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for this shape, or 0 if
+ * B, H or N < 1 or d is not 64 or 128.  It holds, per (b, h), D = rowsum(dO * O) as float32 [N]
+ * (the size is rounded up to 256 bytes). */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward, bf16.  Gradients of L = sum(O * dO) with respect to q, k, v, recomputing S and P
@@ -95,7 +95,7 @@ size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
  *   o, lse      in   the forward's outputs for the same inputs, scale, causal and block_mask
  *   dout        in   bf16 [B, H, N, d]  (dO)
  *   dq, dk, dv  out  bf16 [B, H, N, d]
- *   workspace   scratch of at least flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *   workspace   scratch of at least flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 256-byte
  *               aligned; its contents are undefined afterwards.
  */
 int flash_attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -114,27 +114,32 @@ int flash_attn_bwd_f32(const float *q, const float *k, const float *v, const flo
                        const uint8_t *block_mask, hipStream_t stream);
 
 /* The three stages flash_attn_bwd runs, exposed one by one (bf16) for callers that schedule
- * them themselves or time them separately.  Enqueued in this order on one stream they produce
- * exactly what flash_attn_bwd produces.  Same conventions and checks as flash_attn_bwd; `delta`
- * is a float32 [B, H, N] device tensor, 16-byte aligned.
+ * them themselves or time them separately.  Enqueued in this order on one stream, with one
+ * workspace of at least flash_attn_bwd_workspace_bytes() bytes, they produce exactly what
+ * flash_attn_bwd produces.  Same conventions and checks as flash_attn_bwd.
  *
- * Stage 1: delta_i = sum_c dO_ic * O_ic (the D pre-pass; equals rowsum(P * dP)).
- *   o, dout in bf16 [B, H, N, d]; delta out. */
-int flash_attn_bwd_preprocess(const void *o, const void *dout, float *delta,
+ * Stage 1: the pre-pass over rows: D_i = sum_c dO_ic * O_ic (equals rowsum(P * dP)) and the
+ * feature-major copies of Q and dO, all written into the workspace.
+ *   q, o, dout in bf16 [B, H, N, d]. */
+int flash_attn_bwd_preprocess(const void *q, const void *o, const void *dout,
+                              void *workspace, size_t workspace_bytes,
                               int B, int H, int N, int d, hipStream_t stream);
 
-/* Stage 2: dK and dV, one pass over the query tiles that see each key block
- * (recomputing S and P from lse, [P3 "Innovation #3"]).
- *   q, k, v, dout bf16 in; lse, delta float32 in; dk, dv bf16 out. */
+/* Stage 2: dK and dV, one pass over the query tiles that see each key block (recomputing S and
+ * P from lse, [P3 "Innovation #3"]).  Reads the workspace stage 1 wrote.
+ *   q, k, v, dout bf16 in; lse float32 in; dk, dv bf16 out. */
 int flash_attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
-                        const float *lse, const float *delta, void *dk, void *dv,
+                        const float *lse, const void *workspace, size_t workspace_bytes,
+                        void *dk, void *dv,
                         int B, int H, int N, int d, float scale, int causal,
                         const uint8_t *block_mask, hipStream_t stream);
 
 /* Stage 3: dQ, one pass over the key tiles each query block sees (recomputing S, P and dP).
- *   q, k, v, dout bf16 in; lse, delta float32 in; dq bf16 out. */
+ * Reads the workspace stage 1 wrote.
+ *   q, k, v, dout bf16 in; lse float32 in; dq bf16 out. */
 int flash_attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
-                      const float *lse, const float *delta, void *dq,
+                      const float *lse, const void *workspace, size_t workspace_bytes,
+                      void *dq,
                       int B, int H, int N, int d, float scale, int causal,
                       const uint8_t *block_mask, hipStream_t stream);
 

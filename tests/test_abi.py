@@ -52,9 +52,11 @@ def test_status_strings(L):
 
 def test_workspace_bytes(L):
     import exact_io_aware_flash_amd as fa
-    assert fa.workspace_bytes(1, 1, 1, 64) == 256
-    assert fa.workspace_bytes(2, 3, 100, 128) == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    for B, H, N, d in ((1, 1, 1, 64), (2, 3, 100, 128), (1, 32, 16384, 128), (4, 16, 8192, 64)):
+        assert fa.workspace_bytes(B, H, N, d) == a256(B * H * N * 4), (B, H, N, d)
     assert fa.workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.workspace_bytes(1, 1, 1, 96) == 0
 
 
 # fake, 16-byte aligned, non-overlapping device addresses: never dereferenced by invalid calls
@@ -109,6 +111,7 @@ def test_bwd_argument_errors(L, f32):
     p = ptrs(9)
     ws = ptrs(1, start=1 << 45)[0]
     need = fa.workspace_bytes(1, 1, 128, 64)
+    assert bwd_call(L, p, ctypes.c_void_p(ws.value + 16), need, f32=f32) == fa.FA_ERR_ALIGN
     assert bwd_call(L, p, None, need, f32=f32) == fa.FA_ERR_WORKSPACE
     assert bwd_call(L, p, ws, need - 1, f32=f32) == fa.FA_ERR_WORKSPACE
     for i in range(9):
@@ -139,29 +142,38 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
 
 def test_stage_argument_errors(L):
     import exact_io_aware_flash_amd as fa
-    q, k, v, do, lse, delta, dk, dv, o = ptrs(9)
+    q, k, v, do, lse, ws, dk, dv, o = ptrs(9)
     dims = (1, 1, 128, 64)
-    assert L.flash_attn_bwd_preprocess(None, do, delta, *dims, None) == fa.FA_ERR_NULL
-    assert L.flash_attn_bwd_preprocess(o, do, delta, 1, 1, 128, 32, None) == fa.FA_ERR_HEADDIM
-    assert L.flash_attn_bwd_preprocess(o, do, ctypes.c_void_p(o.value + 16), *dims, None) == fa.FA_ERR_ALIAS
-    args = [q, k, v, do, lse, delta, dk, dv]
-    for i in range(8):
+    need = fa.workspace_bytes(*dims)
+    assert L.flash_attn_bwd_preprocess(None, o, do, ws, need, *dims, None) == fa.FA_ERR_NULL
+    assert L.flash_attn_bwd_preprocess(q, o, do, ws, need, 1, 1, 128, 32, None) == fa.FA_ERR_HEADDIM
+    assert L.flash_attn_bwd_preprocess(q, o, do, ws, need - 1, *dims, None) == fa.FA_ERR_WORKSPACE
+    assert L.flash_attn_bwd_preprocess(q, o, do, ctypes.c_void_p(ws.value + 16), need, *dims,
+                                       None) == fa.FA_ERR_ALIGN
+    assert L.flash_attn_bwd_preprocess(q, o, do, ctypes.c_void_p(o.value + 256), need, *dims,
+                                       None) == fa.FA_ERR_ALIAS
+    args = [q, k, v, do, lse, ws, need, dk, dv]
+    for i in (0, 1, 2, 3, 4, 5, 7, 8):
         a = list(args)
         a[i] = None
         assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_NULL, i
+    assert L.flash_attn_bwd_dkdv(*args[:6], need - 1, *args[7:], *dims, 0.125, 0, None, None) == fa.FA_ERR_WORKSPACE
     assert L.flash_attn_bwd_dkdv(*args, 1, 1, 0, 64, 0.125, 0, None, None) == fa.FA_ERR_SHAPE
     assert L.flash_attn_bwd_dkdv(*args, *dims, 0.0, 0, None, None) == fa.FA_ERR_SCALE
     a = list(args)
-    a[7] = a[6]
+    a[8] = a[7]
     assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
     a = list(args)
-    a[6] = a[4]  # dk over lse
+    a[7] = a[4]  # dk over lse
     assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
-    qargs = [q, k, v, do, lse, delta, dk]
+    a = list(args)
+    a[7] = a[5]  # dk over the workspace
+    assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
+    qargs = [q, k, v, do, lse, ws, need, dk]
     assert L.flash_attn_bwd_dq(*qargs, *dims, 0.125, 3, None, None) == fa.FA_ERR_FLAG
     a = list(qargs)
-    a[6] = ctypes.c_void_p(dk.value + 2)
+    a[7] = ctypes.c_void_p(dk.value + 2)
     assert L.flash_attn_bwd_dq(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIGN
     a = list(qargs)
-    a[6] = a[0]
+    a[7] = a[0]
     assert L.flash_attn_bwd_dq(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS

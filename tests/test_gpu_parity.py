@@ -205,8 +205,8 @@ def test_backward_stages_equal_bwd(dev):
     for causal, bm in ((False, None), (True, None), (True, mask)):
         o, lse = fa.fwd(q, k, v, 0.1, causal, bm)
         dq, dk, dv = fa.bwd(q, k, v, o, lse, do, 0.1, causal, bm)
-        delta = fa.bwd_preprocess(o, do)
-        dk2, dv2 = fa.bwd_dkdv(q, k, v, do, lse, delta, 0.1, causal, bm)
-        dq2 = fa.bwd_dq(q, k, v, do, lse, delta, 0.1, causal, bm)
+        ws = fa.bwd_preprocess(q, o, do)
+        dk2, dv2 = fa.bwd_dkdv(q, k, v, do, lse, ws, 0.1, causal, bm)
+        dq2 = fa.bwd_dq(q, k, v, do, lse, ws, 0.1, causal, bm)
         torch.cuda.synchronize()
         assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
