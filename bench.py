@@ -5,6 +5,15 @@ One step = one forward pass (S = scale Q K^T, online softmax, P V, LSE) and one 
 resident in device memory.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+                    [--copy-calibration MIB]
+    python bench.py --traffic-from FETCH_CSV WRITE_CSV [--workload long]
+
+HBM traffic: run the bench twice under `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` with
+`--copy-calibration 256`, which first copies 256 MiB with the runtime's copy kernel.  The two
+counters read a fixed fraction of the true bytes on this part; the copy of known size gives that
+fraction.  `--traffic-from` turns the two counter files into profiles/hbm_traffic.json (bytes
+per launch of each attention kernel, tagged with a digest of the kernel sources so that a later
+kernel change voids it) and prints a markdown summary.
 
 FLOP convention: forward 4*B*H*N^2*d (halved for causal; block-sparse counts active 128x128
 blocks), backward 2.5x forward.  value = (forward + backward flops) / step time.
@@ -52,8 +61,64 @@ def kernel_flops(w, block_mask):
 
 
 def preprocess_bytes(w):
-    # reads Q, O, dO; writes D (float32) and the feature-major copies of Q and dO
-    return 5 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+    # reads O and dO (bf16), writes D (float32)
+    return 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+
+
+KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_delta_kernel": "bwd_preprocess",
+               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq"}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def read_counter(path: str, counter: str):
+    """{dispatch id: (kernel name, counter value summed over the rows of that dispatch)}."""
+    import csv
+
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = per.get(d, (r["Kernel_Name"], 0.0))
+            per[d] = (name, v + float(r["Counter_Value"]))
+    return per
+
+
+def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_mib: int = 256):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the copy kernel's reading of a copy of
+    known size, write profiles/hbm_traffic.json and return a markdown summary."""
+    import statistics
+
+    copy_bytes = copy_mib * 2 ** 20
+    out = {"csrc_sha256": csrc_digest(), "workload": workload, "copy_bytes": copy_bytes,
+           "sources": [os.path.relpath(fetch_csv, ROOT), os.path.relpath(write_csv, ROOT)], "kernels": []}
+    per_kernel = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = read_counter(path, counter)
+        copies = [v for name, v in vals.values() if COPY_KERNEL in name]
+        if not copies:
+            raise SystemExit(f"{path}: no {COPY_KERNEL} dispatch; run the bench with --copy-calibration {copy_mib}")
+        factor = copy_bytes / (statistics.median(copies) * 1024.0)
+        out[counter.lower() + "_factor"] = factor
+        for name, v in vals.values():
+            for key, short in KERNEL_KEYS.items():
+                if key in name:
+                    per_kernel.setdefault(short, {}).setdefault(counter, []).append(v * 1024.0 * factor)
+    lines = [f"| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | HBM bytes/launch |",
+             "|---|---|---|---|---|"]
+    for short, c in per_kernel.items():
+        fb = statistics.median(c.get("FETCH_SIZE", [0.0]))
+        wb = statistics.median(c.get("WRITE_SIZE", [0.0]))
+        out["kernels"].append({"kernel": short, "workload": workload, "dispatches": len(c.get("FETCH_SIZE", [])),
+                               "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                               "hbm_bytes_per_launch": fb + wb})
+        lines.append(f"| {short} | {len(c.get('FETCH_SIZE', []))} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    head = (f"copy calibration: {copy_mib} MiB copy; FETCH_SIZE factor {out['fetch_size_factor']:.3f}, "
+            f"WRITE_SIZE factor {out['write_size_factor']:.3f}\n\n")
+    return head + "\n".join(lines)
 
 
 def traffic_for(kernel: str, workload: str):
@@ -123,8 +188,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="copy MIB MiB with the runtime's copy kernel before the bench (counter scaling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 counter files and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(traffic_from(*args.traffic_from, workload=args.workload, copy_mib=args.copy_calibration or 256))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -140,6 +212,13 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_gen = time.perf_counter()
     t = workloads.make(w, with_do=not w.fwd_only)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -470,7 +470,8 @@ hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
 template <int D, bool C, bool S>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int nkv = (a.N + 127) / 128;
-  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0);
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, C, S>));
+  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
@@ -478,7 +479,8 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
 template <int D, bool C, bool S>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nq = (a.N + 127) / 128;
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1);
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dq_kernel<D, C, S>));
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }

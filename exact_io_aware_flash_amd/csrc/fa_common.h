@@ -270,15 +270,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------------------------------------
 // Tile scheduler decode.  The grid is one workgroup per (b*h, tile).  Consecutive workgroup ids
-// are dispatched round-robin over the 8 XCDs (each with its own L2); when the item count and
-// B*H are multiples of 8, ids are remapped so that every XCD works through B*H/8 whole heads,
-// keeping a head's K/V (or Q/dO) re-reads inside one L2.  Within a head group the heaviest tiles
-// come first (the causal triangle gives tile t of the query side t + 1 units of work).
+// are dispatched round-robin over the 8 XCDs (each with its own L2); when B*H is a multiple of 8,
+// ids are remapped so that every XCD works through B*H/8 whole heads, keeping a head's K/V (or
+// Q/dO) re-reads inside one L2.  Within an XCD the order is either
+//  - tile-major: tile level by tile level, heaviest level first, all the XCD's heads at each level
+//    (best balance when a head has few tiles: the causal triangle gives query tile t t + 1 units
+//    of work, so the long tiles must start first), or
+//  - head-major: one head after another, each heaviest tile first, so that the workgroups in
+//    flight on an XCD stream the same head's K/V tiles at about the same time and share them in
+//    L2 (used when a head has enough tiles to fill the XCD's slots twice over, where the late
+//    start of the last head's long tiles is a small tail).
 // ---------------------------------------------------------------------------------------------
 struct Sched {
-  int ntiles;  // tiles per head
-  int group;   // heads per XCD group (divides B*H)
-  int remap;   // 1: XCD-aware remap active
+  int ntiles;      // tiles per head
+  int group;       // heads per XCD group (divides B*H)
+  int remap;       // 1: XCD-aware remap active
+  int head_major;  // 1: head-major order inside a group (needs remap)
   int heavy_last_tile;  // 1: tile ntiles-1 is the heaviest (query side); 0: tile 0 is
 };
 
@@ -288,9 +295,16 @@ __device__ __forceinline__ void sched_decode(const Sched& s, int total, int& bh,
   const int per = s.group * s.ntiles;
   const int hg = w / per;
   const int r = w - hg * per;
-  const int t = r / s.group;
+  int t, hh;
+  if (s.head_major) {
+    hh = r / s.ntiles;
+    t = r - hh * s.ntiles;
+  } else {
+    t = r / s.group;
+    hh = r - t * s.group;
+  }
   tile = s.heavy_last_tile ? (s.ntiles - 1 - t) : t;
-  bh = hg * s.group + (r - t * s.group);
+  bh = hg * s.group + hh;
 }
 
 // Builds, in LDS, the ascending list of mask blocks J with block_mask[I][J] != 0 (row mode) or

@@ -57,16 +57,30 @@ struct F32Args {
   float scale;
 };
 
-inline Sched make_sched(int ntiles, int BH, int heavy_last_tile) {
+// Workgroups of 256 threads of `kernel` resident at once on one XCD: occupancy per CU times the
+// CUs of one of the 8 XCDs.  Asked once per kernel instantiation (the caller caches it).
+inline int xcd_slots(const void* kernel) {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  (void)hipGetLastError();  // a failed query must not surface as the launch's error
+  return per_cu * (cus / 8);
+}
+
+inline Sched make_sched(int ntiles, int BH, int heavy_last_tile, int slots_per_xcd) {
   Sched s;
   s.ntiles = ntiles;
   s.heavy_last_tile = heavy_last_tile;
   if (BH % 8 == 0) {
     s.remap = 1;
     s.group = BH / 8;
+    s.head_major = ntiles >= 2 * slots_per_xcd;
   } else {
     s.remap = 0;
     s.group = BH;
+    s.head_major = 0;
   }
   return s;
 }

@@ -249,23 +249,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
 }  // namespace
 
 template <int D, bool C, bool S>
-static hipError_t launch_fwd_t(const FwdArgs& a, const Sched& sc, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S>), dim3(grid), dim3(256), 0, st, a, sc);
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  constexpr int BR = 128;
+  const int nq = (a.N + BR - 1) / BR;
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S>));
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BR = 128;
-  const int nq = (a.N + BR - 1) / BR;
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1);
-  const int grid = nq * a.BH;
   const bool causal = a.causal != 0, sparse = a.mask != nullptr;
   if (a.d == 64) {
-    if (causal) return sparse ? launch_fwd_t<64, true, true>(a, sc, grid, stream) : launch_fwd_t<64, true, false>(a, sc, grid, stream);
-    return sparse ? launch_fwd_t<64, false, true>(a, sc, grid, stream) : launch_fwd_t<64, false, false>(a, sc, grid, stream);
+    if (causal) return sparse ? launch_fwd_t<64, true, true>(a, stream) : launch_fwd_t<64, true, false>(a, stream);
+    return sparse ? launch_fwd_t<64, false, true>(a, stream) : launch_fwd_t<64, false, false>(a, stream);
   }
-  if (causal) return sparse ? launch_fwd_t<128, true, true>(a, sc, grid, stream) : launch_fwd_t<128, true, false>(a, sc, grid, stream);
-  return sparse ? launch_fwd_t<128, false, true>(a, sc, grid, stream) : launch_fwd_t<128, false, false>(a, sc, grid, stream);
+  if (causal) return sparse ? launch_fwd_t<128, true, true>(a, stream) : launch_fwd_t<128, true, false>(a, stream);
+  return sparse ? launch_fwd_t<128, false, true>(a, stream) : launch_fwd_t<128, false, false>(a, stream);
 }
 
 }  // namespace fa

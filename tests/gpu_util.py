@@ -87,13 +87,18 @@ def run_lib(t: workloads.Tensors, scale, causal, dev, backward=True):
     k = to_dev(t.k, t.dtype, dev)
     v = to_dev(t.v, t.dtype, dev)
     mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
-    o, lse = fa.fwd(q, k, v, scale, causal, mask)
+    # outputs start as NaN, so that an element no workgroup wrote is caught on every size
+    nan = lambda shape, dt: torch.full(shape, float("nan"), dtype=dt, device=dev)
+    o, lse = fa.fwd(q, k, v, scale, causal, mask, out=nan(q.shape, q.dtype), lse=nan(q.shape[:3], torch.float32))
     out = {"o": o, "lse": lse}
     if backward:
         do = to_dev(t.do, t.dtype, dev)
-        dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale, causal, mask)
+        dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale, causal, mask, dq=nan(q.shape, q.dtype),
+                            dk=nan(q.shape, q.dtype), dv=nan(q.shape, q.dtype))
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
+    for name, x in out.items():
+        assert not torch.isnan(x).any().item(), f"{name}: elements left unwritten (or NaN) on the device"
     return out
 
 

@@ -67,6 +67,16 @@ def test_long_context_64k_forward_sampled(dev):
     _run_and_compare("long64k fwd", t, w.scale, w.causal, dev, heads=[(0, 0), (0, 7)], backward=False, rows=rows)
 
 
+def test_head_major_schedule_sampled(dev):
+    """B*H = 16 heads of N = 8192, d = 128, causal: the dK/dV grid has enough key tiles per head to
+    run its XCD groups head by head, while the forward and dQ grids run tile level by tile level."""
+    t = workloads.random_case(2, 8, 8192, 128, "bf16", seed=900)
+    rows = G.sample_rows(8192, 40, seed=901)
+    cols = G.sample_rows(8192, 40, seed=902)
+    _run_and_compare("head-major N=8192 d=128", t, 1.0 / math.sqrt(128), True, dev, heads=[(0, 0), (1, 7)],
+                     rows=rows, cols=cols)
+
+
 def test_block_sparse(dev):
     w = workloads.WORKLOADS["sparse"]
     t = workloads.make(w)
