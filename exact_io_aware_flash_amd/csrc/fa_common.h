@@ -117,25 +117,34 @@ __device__ __forceinline__ void dma16(const Rsrc& r, void* lds_block, int voff, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds_block, 16, voff, soff, 0, 0);
 }  // soff stays 0 in this library: the range check does not cover it
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// 16-byte chunk swizzle (row = tile row, D = row length in bf16), good for both read patterns:
-//  row reads: 16 lanes read the same logical chunk of 16 consecutive rows -> 16 distinct slots
-//             of the 256-byte bank window (d = 128: one row per window, f is a bijection on
-//             row bits 0-3; d = 64: two rows per window, f is a bijection on row bits 1-3);
-//  transposed reads: 16 lanes read 2 adjacent chunks of 4 consecutive rows -> the 4 chunk pairs
-//             land on distinct pairs of slots (f >> 1 differs across the rows sharing a window).
-template <int D>
-__device__ __forceinline__ constexpr int sw_dual(int row) {
-  return D >= 128 ? (2 * (row & 3) + ((row >> 2) & 1) + 8 * ((row >> 3) & 1))
-                  : (2 * ((row >> 1) & 1) + 4 * ((row >> 2) & 1) + ((row >> 3) & 1));
+// wait until at most N of this wave's vector-memory instructions (copies included) are in
+// flight; they complete in issue order, so everything issued before the last N has landed
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int R, int D>
+// 16-byte chunk swizzle (row = tile row, D = row length in bf16), free of LDS bank conflicts
+// for both read patterns (64 banks x 4 bytes = one 256-byte window of 16 chunk slots):
+//  row reads (16 bytes per lane, 16 lanes per cycle): the lanes read one logical chunk of 16
+//             rows, so f must be a bijection on rows 0..15 (d = 64: two rows share a window,
+//             so on the 8 even and on the 8 odd rows);
+//  transposed reads (8 bytes per lane, 32 lanes per cycle): the lanes read 4 logical chunks
+//             (an aligned group of 4) of 4 consecutive rows 4u .. 4u+3, so the rows sharing a
+//             window must move the group to different aligned slots: f & 12 distinct across
+//             them (d = 64: bit 2 of f distinct between rows 4u and 4u+2, 4u+1 and 4u+3).
+template <int D>
+__device__ __forceinline__ constexpr int sw_dual(int row) {
+  return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+template <int R, int D, int NW = 4>
 struct DmaTile {
   static constexpr int CPR = D / 8;
   static constexpr int BYTES = R * D * 2;
-  static constexpr int CH = R * CPR / 256;  // instructions per wave (4 waves)
-  static_assert(CH >= 1 && (R * CPR) % 256 == 0, "tile too small for 4 waves");
+  static constexpr int CH = R * CPR / (64 * NW);  // instructions per wave (NW waves)
+  static_assert(CH >= 1 && (R * CPR) % (64 * NW) == 0, "tile too small for the waves");
   __device__ static constexpr int sw(int row) { return sw_dual<D>(row); }
   // byte offset in the tile of the 16-byte chunk holding (row, col), col a multiple of 8
   __device__ static constexpr int off(int row, int col) { return row * D * 2 + (((col >> 3) ^ sw(row)) << 4); }

@@ -57,11 +57,13 @@ struct F32Args {
   float scale;
 };
 
-// Workgroups of 256 threads of `kernel` resident at once on one XCD: occupancy per CU times the
-// CUs of one of the 8 XCDs.  Asked once per kernel instantiation (the caller caches it).
-inline int xcd_slots(const void* kernel) {
+// Workgroups of `kernel` (block_threads threads each) resident at once on one XCD: occupancy
+// per CU times the CUs of one of the 8 XCDs.  Asked once per kernel instantiation (the caller
+// caches it).
+inline int xcd_slots(const void* kernel, int block_threads = 256) {
   int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
     cus = 256;

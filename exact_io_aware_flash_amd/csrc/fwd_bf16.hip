@@ -122,13 +122,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   vdma.init(w, lane);
 
   // S^T = K Q^T for two 32-key blocks; register r of half h holds key k0 + 32 kb + acc_row(r, h)
+  // the two 32-key blocks alternate, so consecutive MFMAs are independent; K reads run four
+  // MFMAs ahead of their use (the scheduling groups keep the compiler from sinking them)
   auto scores = [&](const char* tk, f32x16(&s)[2]) {
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
+    for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int c = 0; c < DC; ++c) s[kb] = mfma32(lds_b128(tk + kaddr[c] + 32 * kb * D * 2), qreg[c], s[kb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(lds_b128(tk + kaddr[c] + 32 * kb * D * 2), qreg[c], s[kb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DC - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // Software pipeline over key tiles (K runs one tile ahead of V):
@@ -214,6 +223,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
         const char* vb = v_cur + 16 * m * D * 2;
         oacc[db] = mfma32(join8(lds_tr4(vb + vaddr[0][db]), lds_tr4(vb + vaddr[1][db])), pk[m], oacc[db]);
       }
+    // each PV MFMA takes one transposed operand (two 8-byte reads), kept two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 
     wait_dma();
     __syncthreads();
