@@ -26,7 +26,9 @@ FA_ERR_WORKSPACE = 6
 FA_ERR_HIP = 7
 FA_ERR_ALIAS = 8
 FA_ERR_FLAG = 9
+FA_ERR_SPLITS = 10
 MASK_BLOCK = 128
+MAX_SPLITS = 64
 
 _lib = None
 
@@ -62,6 +64,12 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_bwd_dkdv.restype = i
     L.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_bwd_dq.restype = i
+    L.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.flash_attn_fwd_splitkv_workspace_bytes.restype = sz
+    L.flash_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp]
+    L.flash_attn_fwd_splitkv.restype = i
+    L.flash_attn_merge.argtypes = [vp, vp, i, ctypes.c_int64, i, vp, vp, vp]
+    L.flash_attn_merge.restype = i
     L.flash_attn_status_string.argtypes = [i]
     L.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -177,6 +185,74 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, b
     return dq, dk, dv
 
 
+def splitkv_workspace_bytes(B: int, H: int, N: int, d: int, splits: int) -> int:
+    return int(lib().flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits))
+
+
+def default_splits(B: int, H: int, N: int) -> int:
+    """Key ranges for fwd_splitkv when the caller gives none: enough that the grid has about
+    1024 workgroups (four per compute unit), at most 8; 1 when the plain grid already has that."""
+    wgs = B * H * ((N + 127) // 128)
+    s = 1
+    while s < 8 and wgs * s < 1024:
+        s *= 2
+    return s
+
+
+def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, block_mask=None, splits: int | None = None,
+                out=None, lse=None, workspace=None, stream=None):
+    """Split-key forward (bf16): the key blocks are cut into `splits` ranges whose partial
+    results are merged by log-sum-exp.  Same result as fwd() up to rounding order.
+    Returns (o, lse)."""
+    import torch
+
+    B, H, N, d = q.shape
+    if splits is None:
+        splits = default_splits(B, H, N)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    if workspace is None:
+        need = splitkv_workspace_bytes(B, H, N, d, splits)
+        if need == 0:
+            raise FlashAttnError(FA_ERR_SPLITS, "fwd_splitkv")
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                      int(bool(causal)), _ptr(bm), int(splits), _ptr(workspace), _ws_bytes(workspace),
+                                      _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_splitkv")
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Log-sum-exp merge of partial results over disjoint key sets of the same rows:
+    o_parts float32 [P, ..., d], lse_parts float32 [P, ...] -> (o bf16 [..., d], lse float32 [...])."""
+    import torch
+
+    P = o_parts.shape[0]
+    rows_shape = tuple(o_parts.shape[1:-1])
+    d = o_parts.shape[-1]
+    dev = o_parts.device
+    _check(o_parts, "o_parts", torch.float32, (P, *rows_shape, d), dev)
+    _check(lse_parts, "lse_parts", torch.float32, (P, *rows_shape), dev)
+    out = torch.empty((*rows_shape, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty(rows_shape, dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, (*rows_shape, d), dev)
+    _check(lse, "lse", torch.float32, rows_shape, dev)
+    rows = int(math.prod(rows_shape))
+    st = lib().flash_attn_merge(_ptr(o_parts), _ptr(lse_parts), P, rows, d, _ptr(out), _ptr(lse), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_merge")
+    return out, lse
+
+
 # ---------------------------------------------------------------------------------------------
 # The three backward stages one by one (bf16).  Enqueued in this order with one workspace they
 # equal bwd().
@@ -244,3 +320,42 @@ def bwd_dq(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=Non
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_dq")
     return dq
+
+
+# ---------------------------------------------------------------------------------------------
+# Autograd entry: O = attention(Q, K, V) as a differentiable PyTorch operation.  The forward
+# keeps O and LSE for the backward, which recomputes S and P tile by tile from them (the
+# recomputation of the backward pass: "How FlashAttention Eliminates Transformer Memory
+# Bottlenecks", Innovation #3).  Both directions run in the library's kernels.
+def _attention_fn():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, scale, causal, block_mask):
+            o, lse = fwd(q, k, v, scale, causal, block_mask)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.scale, ctx.causal, ctx.block_mask = scale, causal, block_mask
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal, ctx.block_mask)
+            return dq, dk, dv, None, None, None
+
+    return _Attention
+
+
+_ATTENTION = None
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False, block_mask=None):
+    """Differentiable exact attention: returns O [B, H, N, d] (input dtype) for q, k, v of shape
+    [B, H, N, d] (bf16 or float32, contiguous, on the GPU); gradients flow to q, k and v."""
+    global _ATTENTION
+    if _ATTENTION is None:
+        _ATTENTION = _attention_fn()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _ATTENTION.apply(q, k, v, float(scale), bool(causal), block_mask)

@@ -123,6 +123,31 @@ int stage_checked(const void* const* in, const long long* in_bytes, int nin, voi
   return check_alias(ri, nin + 1, ro, nout);
 }
 
+fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                     float scale, int causal, const uint8_t* block_mask) {
+  fa::FwdArgs a = {};
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.mask = block_mask;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * fa::kLog2e;
+  a.splits = 1;
+  return a;
+}
+
+size_t splitkv_workspace_bytes(int B, int H, int N, int d, int splits) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || splits < 1 || splits > FA_MAX_SPLITS) return 0;
+  return fa::splitkv_ws_bytes((long long)B * H, N, d, splits);
+}
+
 fa::BwdArgs stage_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, const void* workspace, void* dq, void* dk, void* dv, int B, int H, int N,
                        int d, float scale, int causal, const uint8_t* block_mask) {
@@ -164,6 +189,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_HIP: return "a HIP kernel launch failed";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
+    case FA_ERR_SPLITS: return "splits / parts must be in 1 .. FA_MAX_SPLITS";
     default: return "unknown status";
   }
 }
@@ -179,21 +205,51 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
   __bf16* ob = static_cast<__bf16*>(o);
   int st = fwd_checked(qb, kb, vb, ob, lse, B, H, N, d, scale, causal, block_mask, true, &elems);
   if (st != FA_OK) return st;
-  fa::FwdArgs a;
-  a.q = qb;
-  a.k = kb;
-  a.v = vb;
-  a.o = ob;
-  a.lse = lse;
-  a.mask = block_mask;
-  a.N = N;
-  a.d = d;
-  a.BH = B * H;
-  a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
-  a.causal = causal;
-  a.scale = scale;
-  a.scale_log2 = scale * fa::kLog2e;
-  return status_of(fa::launch_fwd_bf16(a, stream));
+  return status_of(fa::launch_fwd_bf16(fwd_args(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask), stream));
+}
+
+size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int splits) {
+  return splitkv_workspace_bytes(B, H, N, d, splits);
+}
+
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, float scale, int causal, const uint8_t* block_mask, int splits, void* workspace,
+                           size_t workspace_bytes_, hipStream_t stream) {
+  long long elems = 0;
+  int st = fwd_checked(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                       static_cast<__bf16*>(o), lse, B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  if (splits < 1 || splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  const size_t need = splitkv_workspace_bytes(B, H, N, d, splits);
+  if (!workspace || workspace_bytes_ < need) return FA_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return FA_ERR_ALIGN;
+  const long long tb = elems * 2, lb = (long long)B * H * N * 4;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[4] = {rng(q, tb), rng(k, tb), rng(v, tb), rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[3] = {rng(o, tb), rng(lse, lb), rng(workspace, (long long)need)};
+  st = check_alias(in, 4, out, 3);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a = fwd_args(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask);
+  a.splits = splits;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        fa::splitkv_o_bytes((long long)B * H, N, d, splits));
+  return status_of(fa::launch_fwd_splitkv_bf16(a, stream));
+}
+
+int flash_attn_merge(const float* o_parts, const float* lse_parts, int parts, int64_t rows, int d, void* o,
+                     float* lse, hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (rows < 1 || rows >= kMaxElems / 1024) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (parts < 1 || parts > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const long long ob = (long long)parts * rows * d * 4, lb = (long long)parts * rows * 4;
+  Range in[2] = {rng(o_parts, ob), rng(lse_parts, lb)};
+  Range out[2] = {rng(o, rows * d * 2), rng(lse, rows * 4)};
+  int st = check_alias(in, 2, out, 2);
+  if (st != FA_OK) return st;
+  return status_of(fa::launch_merge_bf16(o_parts, lse_parts, parts, rows, d, static_cast<__bf16*>(o), lse, stream));
 }
 
 int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,

@@ -19,7 +19,21 @@ struct FwdArgs {
   int N, d, BH, nb, causal;
   float scale;       // natural-units scale
   float scale_log2;  // scale * log2(e)
+  // split-key forward: the 128-key blocks are cut into `splits` contiguous ranges (range s =
+  // blocks [s * nb / splits, (s + 1) * nb / splits)); range s writes its normalised partial
+  // output to o_part[s] (float32 [BH, N, d]) and its log-sum-exp to lse_part[s] ([BH, N])
+  int splits;
+  float* o_part;
+  float* lse_part;
 };
+
+// Split-key forward workspace: float32 partial outputs [splits, BH, N, d] followed by partial
+// log-sum-exps [splits, BH, N], each part 256-byte aligned.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t splitkv_o_bytes(long long BH, int N, int d, int splits) { return align256((size_t)splits * BH * N * d * 4); }
+inline size_t splitkv_ws_bytes(long long BH, int N, int d, int splits) {
+  return splitkv_o_bytes(BH, N, d, splits) + align256((size_t)splits * BH * N * 4);
+}
 
 struct BwdArgs {
   const __bf16* q;
@@ -88,6 +102,11 @@ inline Sched make_sched(int ntiles, int BH, int heavy_last_tile, int slots_per_x
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// split-key forward: partials into a.o_part / a.lse_part, then the log-sum-exp merge into a.o / a.lse
+hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, hipStream_t stream);
+// log-sum-exp merge of `parts` partial results over disjoint key sets of the same `rows` rows
+hipError_t launch_merge_bf16(const float* o_parts, const float* lse_parts, int parts, long long rows, int d,
+                             __bf16* o, float* lse, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream);

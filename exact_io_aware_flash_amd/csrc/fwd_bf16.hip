@@ -37,7 +37,7 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   constexpr int BR = 128, BC = 64;
   constexpr int DC = D / 16;  // 16-wide contraction chunks over d
@@ -62,15 +62,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   const __bf16* __restrict__ K = a.k + base;
   const __bf16* __restrict__ V = a.v + base;
 
-  // ---- key tiles this query block visits
+  // ---- key tiles this query block visits: all of them, or (split-key forward) those of the
+  // 128-key blocks [blo, bhi) of range blockIdx.y
   const int nk = (N + BC - 1) / BC;
-  int ntiles = nk;
-  if (CAUSAL) ntiles = min(nk, (min(q0 + BR, N) - 1) / BC + 1);
+  const int blo = SPLIT ? (int)((long long)blockIdx.y * a.nb / a.splits) : 0;
+  const int bhi = SPLIT ? (int)((long long)(blockIdx.y + 1) * a.nb / a.splits) : a.nb;
+  const int tlo = 2 * blo;
+  int tend = SPLIT ? min(nk, 2 * bhi) : nk;  // one past the last tile
+  if (CAUSAL) tend = min(tend, (min(q0 + BR, N) - 1) / BC + 1);
+  int ntiles = max(tend - tlo, 0);
   if (SPARSE) {
     const int qb = q0 / kMaskBlock;
-    const int hi = CAUSAL ? qb + 1 : a.nb;
+    const int hi = CAUSAL ? min(qb + 1, bhi) : bhi;
     if (w == 0) {
-      const int cnt = build_block_list(a.mask, a.nb, qb, false, 0, hi, blist, lane);
+      const int cnt = build_block_list(a.mask, a.nb, qb, false, blo, hi, blist, lane);
       if (lane == 0) bcount = cnt;
     }
     __syncthreads();
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   }
   auto tile_start = [&](int t) -> int {
     if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
-    return t * BC;
+    return (tlo + t) * BC;
   };
 
   // ---- Q^T operand in registers (B operand: lane holds query q0 + 32w + c32, features 16c + 8h ..)
@@ -248,6 +253,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   // ---- epilogue: lane holds features 32 db + 8 g + 4 h + e of query qrow in register 4 g + e
   const float ltot = half_swap_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (SPLIT) {
+    if (qrow < N) {
+      const size_t prow = ((size_t)blockIdx.y * a.BH + bh) * N + qrow;
+      float* orow = a.o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = oacc[db][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = v4;
+        }
+      if (h == 0) a.lse_part[prow] = ltot > 0.f ? (m_used + __log2f(ltot)) * kLn2 : neg_inf();
+    }
+    return;
+  }
   if (qrow < N) {
     __bf16* orow = a.o + base + (size_t)qrow * D;
 #pragma unroll
@@ -261,6 +283,42 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
       }
     if (h == 0) a.lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m_used + __log2f(ltot)) * kLn2 : neg_inf();
   }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// Log-sum-exp merge of partial results over disjoint key sets of the same query rows: with
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s, which is the softmax over the union
+// of the key sets (each O_s is already normalised by its own sum).  Rows whose parts are all
+// dead (LSE_s = -inf) get O = 0 and LSE = -inf.  TPR threads per row, 4 features per thread.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
+                                                    int parts, long long rows, __bf16* __restrict__ o,
+                                                    float* __restrict__ lse) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int f = 4 * (threadIdx.x % TPR);
+  if (row >= rows) return;
+  float m = neg_inf();
+  for (int s = 0; s < parts; ++s) m = fmaxf(m, lse_parts[(size_t)s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != neg_inf()) {
+    for (int s = 0; s < parts; ++s) {
+      const float ls = lse_parts[(size_t)s * rows + row];
+      const float wt = fast_exp2((ls - m) * kLog2e);  // 0 for a dead part
+      wsum += wt;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(o_parts + ((size_t)s * rows + row) * D + f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wt, v[e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(o + (size_t)row * D + f) = out;
+  if (f == 0) lse[row] = wsum > 0.f ? m + __logf(wsum) : neg_inf();
 }
 
 }  // namespace
@@ -283,6 +341,41 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   }
   if (causal) return sparse ? launch_fwd_t<128, true, true>(a, stream) : launch_fwd_t<128, true, false>(a, stream);
   return sparse ? launch_fwd_t<128, false, true>(a, stream) : launch_fwd_t<128, false, false>(a, stream);
+}
+
+template <int D, bool C, bool S>
+static hipError_t launch_splitkv_t(const FwdArgs& a, hipStream_t st) {
+  constexpr int BR = 128;
+  const int nq = (a.N + BR - 1) / BR;
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S, true>));
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S, true>), dim3(nq * a.BH, a.splits), dim3(256), 0, st, a, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_bf16(const float* o_parts, const float* lse_parts, int parts, long long rows, int d,
+                             __bf16* o, float* lse, hipStream_t st) {
+  const int rpb = 256 / (d / 4);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (d == 64)
+    hipLaunchKernelGGL((merge_kernel<64>), dim3(grid), dim3(256), 0, st, o_parts, lse_parts, parts, rows, o, lse);
+  else
+    hipLaunchKernelGGL((merge_kernel<128>), dim3(grid), dim3(256), 0, st, o_parts, lse_parts, parts, rows, o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, hipStream_t stream) {
+  const bool causal = a.causal != 0, sparse = a.mask != nullptr;
+  hipError_t e;
+  if (a.d == 64) {
+    if (causal) e = sparse ? launch_splitkv_t<64, true, true>(a, stream) : launch_splitkv_t<64, true, false>(a, stream);
+    else e = sparse ? launch_splitkv_t<64, false, true>(a, stream) : launch_splitkv_t<64, false, false>(a, stream);
+  } else {
+    if (causal) e = sparse ? launch_splitkv_t<128, true, true>(a, stream) : launch_splitkv_t<128, true, false>(a, stream);
+    else e = sparse ? launch_splitkv_t<128, false, true>(a, stream) : launch_splitkv_t<128, false, false>(a, stream);
+  }
+  if (e != hipSuccess) return e;
+  return launch_merge_bf16(a.o_part, a.lse_part, a.splits, (long long)a.BH * a.N, a.d, a.o, a.lse, stream);
 }
 
 }  // namespace fa

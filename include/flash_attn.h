@@ -47,6 +47,7 @@ extern "C" {
 
 #define FA_MASK_BLOCK 128
 #define FA_MAX_MASK_BLOCKS 2048
+#define FA_MAX_SPLITS 64
 
 enum {
   FA_OK = 0,
@@ -58,7 +59,8 @@ enum {
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than flash_attn_bwd_workspace_bytes() */
   FA_ERR_HIP = 7,       /* a kernel launch failed */
   FA_ERR_ALIAS = 8,     /* an output overlaps an input or another output */
-  FA_ERR_FLAG = 9       /* causal not 0 or 1 */
+  FA_ERR_FLAG = 9,      /* causal not 0 or 1 */
+  FA_ERR_SPLITS = 10    /* splits / parts not in 1 .. FA_MAX_SPLITS */
 };
 
 /* Forward, bf16 inputs and outputs, fp32 accumulation.
@@ -81,6 +83,41 @@ int flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *
 int flash_attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                        int B, int H, int N, int d, float scale, int causal,
                        const uint8_t *block_mask, hipStream_t stream);
+
+/* Split-key forward, bf16 (the sequence-parallel form of the forward: "How FlashAttention
+ * Bypasses the GPU Memory Bottleneck to Enable Long-Context AI" on parallelising over the
+ * sequence length).  The 128-key blocks of every (b, h) are cut into `splits` contiguous ranges
+ * (range s = blocks [s * nb / splits, (s + 1) * nb / splits), nb = ceil(N / 128)); each range
+ * computes its own normalised partial output O_s and log-sum-exp LSE_s over its keys, and the
+ * partials are merged exactly as flash_attn_merge does.  The result is flash_attn_fwd's up to
+ * floating-point rounding order (not bit-identical).  Worth it when B * H * ceil(N / 128) is
+ * small against the GPU's 256 compute units, or when one query block's key range is long.
+ *   q, k, v, o, lse, scale, causal, block_mask   as flash_attn_fwd
+ *   splits      1 .. FA_MAX_SPLITS (else FA_ERR_SPLITS)
+ *   workspace   at least flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) bytes,
+ *               256-byte aligned, owned by the caller; holds the float32 partials
+ *               ([splits, B, H, N, d] outputs, then [splits, B, H, N] log-sum-exps); contents
+ *               undefined afterwards.  Must not overlap any input or output (FA_ERR_ALIAS).
+ */
+size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int splits);
+int flash_attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t *block_mask, int splits,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Log-sum-exp merge of `parts` partial results computed over disjoint key sets of the same
+ * query rows (the partials of a split-key forward, or of key shards held by different
+ * devices).  Per row: LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, the softmax
+ * over the union of the key sets; a part with LSE_s = -inf (no visible key) contributes nothing,
+ * and a row whose parts are all -inf gets O = 0, LSE = -inf.
+ *   o_parts    in   float32 [parts, rows, d], each O_s normalised by its own sum
+ *   lse_parts  in   float32 [parts, rows], natural log
+ *   parts      1 .. FA_MAX_SPLITS;  rows >= 1;  d in {64, 128}
+ *   o          out  bf16 [rows, d] (round to nearest even)
+ *   lse        out  float32 [rows]
+ */
+int flash_attn_merge(const float *o_parts, const float *lse_parts, int parts, int64_t rows, int d,
+                     void *o, float *lse, hipStream_t stream);
 
 /* Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for this shape, or 0 if
  * B, H or N < 1 or d is not 64 or 128.  It holds, per (b, h), D = rowsum(dO * O) as float32 [N]
@@ -118,9 +155,9 @@ int flash_attn_bwd_f32(const float *q, const float *k, const float *v, const flo
  * workspace of at least flash_attn_bwd_workspace_bytes() bytes, they produce exactly what
  * flash_attn_bwd produces.  Same conventions and checks as flash_attn_bwd.
  *
- * Stage 1: the pre-pass over rows: D_i = sum_c dO_ic * O_ic (equals rowsum(P * dP)) and the
- * feature-major copies of Q and dO, all written into the workspace.
- *   q, o, dout in bf16 [B, H, N, d]. */
+ * Stage 1: the pre-pass over rows: D_i = sum_c dO_ic * O_ic (equals rowsum(P * dP)), written
+ * into the workspace as float32 [B, H, N].
+ *   q, o, dout in bf16 [B, H, N, d]; q is checked like the others but not read. */
 int flash_attn_bwd_preprocess(const void *q, const void *o, const void *dout,
                               void *workspace, size_t workspace_bytes,
                               int B, int H, int N, int d, hipStream_t stream);

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_f32", "flash_attn_bwd_f32",
               "flash_attn_bwd_workspace_bytes", "flash_attn_status_string", "flash_attn_bwd_preprocess",
-              "flash_attn_bwd_dkdv", "flash_attn_bwd_dq"):
+              "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_fwd_splitkv",
+              "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_merge"):
         assert n in names, n
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_status_strings(L):
     import exact_io_aware_flash_amd as fa
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa.status_string(code)
         assert s and s != "unknown status", code
     assert fa.status_string(12345) == "unknown status"
@@ -177,3 +178,55 @@ def test_stage_argument_errors(L):
     a = list(qargs)
     a[7] = a[0]
     assert L.flash_attn_bwd_dq(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
+
+
+def test_splitkv_workspace_bytes(L):
+    import exact_io_aware_flash_amd as fa
+    a256 = lambda x: (x + 255) // 256 * 256
+    for B, H, N, d, S in ((1, 1, 1, 64, 1), (2, 3, 100, 128, 3), (1, 32, 16384, 128, 4), (1, 1, 300, 64, 64)):
+        want = a256(S * B * H * N * d * 4) + a256(S * B * H * N * 4)
+        assert fa.splitkv_workspace_bytes(B, H, N, d, S) == want, (B, H, N, d, S)
+    assert fa.splitkv_workspace_bytes(1, 1, 128, 64, 0) == 0
+    assert fa.splitkv_workspace_bytes(1, 1, 128, 64, fa.MAX_SPLITS + 1) == 0
+    assert fa.splitkv_workspace_bytes(1, 1, 128, 96, 2) == 0
+
+
+def test_splitkv_argument_errors(L):
+    import exact_io_aware_flash_amd as fa
+    q, k, v, o, lse, m = ptrs(6)
+    ws = ptrs(1, start=1 << 45)[0]
+    need = fa.splitkv_workspace_bytes(1, 1, 128, 64, 2)
+
+    def call(q=q, o=o, lse=lse, ws=ws, wsb=need, N=128, d=64, scale=0.125, causal=0, mask=None, splits=2):
+        return L.flash_attn_fwd_splitkv(q, k, v, o, lse, 1, 1, N, d, scale, causal, mask, splits, ws, wsb, None)
+
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(d=96) == fa.FA_ERR_HEADDIM
+    assert call(scale=float("nan")) == fa.FA_ERR_SCALE
+    assert call(causal=5) == fa.FA_ERR_FLAG
+    assert call(splits=0) == fa.FA_ERR_SPLITS
+    assert call(splits=fa.MAX_SPLITS + 1) == fa.FA_ERR_SPLITS
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(ws.value + 128)) == fa.FA_ERR_ALIGN
+    assert call(ws=k) == fa.FA_ERR_ALIAS  # workspace over an input
+    assert call(ws=ctypes.c_void_p(o.value + 256)) == fa.FA_ERR_ALIAS  # workspace over the output
+    assert call(o=q) == fa.FA_ERR_ALIAS
+
+
+def test_merge_argument_errors(L):
+    import exact_io_aware_flash_amd as fa
+    op, lp, o, lse = ptrs(4)
+
+    def call(op=op, lp=lp, parts=2, rows=100, d=64, o=o, lse=lse):
+        return L.flash_attn_merge(op, lp, parts, rows, d, o, lse, None)
+
+    assert call(op=None) == fa.FA_ERR_NULL
+    assert call(lse=None) == fa.FA_ERR_NULL
+    assert call(parts=0) == fa.FA_ERR_SPLITS
+    assert call(parts=fa.MAX_SPLITS + 1) == fa.FA_ERR_SPLITS
+    assert call(rows=0) == fa.FA_ERR_SHAPE
+    assert call(d=32) == fa.FA_ERR_HEADDIM
+    assert call(o=ctypes.c_void_p(o.value + 8)) == fa.FA_ERR_ALIGN
+    assert call(o=ctypes.c_void_p(op.value + 1024)) == fa.FA_ERR_ALIAS
+    assert call(lse=ctypes.c_void_p(o.value + 64)) == fa.FA_ERR_ALIAS

@@ -220,3 +220,101 @@ def test_backward_stages_equal_bwd(dev):
         dq2 = fa.bwd_dq(q, k, v, do, lse, ws, 0.1, causal, bm)
         torch.cuda.synchronize()
         assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_autograd_wrapper(dev):
+    """attention() as a torch.autograd operation: its forward equals fwd() and its gradients equal
+    bwd() bit for bit, and both match the oracle."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(1, 2, 300, 64, "bf16", seed=1100)
+    q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o = fa.attention(qa, ka, va, 0.125, True)
+    o.backward(do)
+    o_ref, lse_ref = fa.fwd(q, k, v, 0.125, True)
+    dq_ref, dk_ref, dv_ref = fa.bwd(q, k, v, o_ref, lse_ref, do, 0.125, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    assert torch.equal(qa.grad, dq_ref) and torch.equal(ka.grad, dk_ref) and torch.equal(va.grad, dv_ref)
+    res = {"o": o.detach(), "lse": lse_ref, "dq": qa.grad, "dk": ka.grad, "dv": va.grad}
+    G.compare_heads(t, res, 0.125, True, heads=[(0, 0), (0, 1)])
+
+
+# ------------------------------------------------------------------------------ split-key forward
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", ["dense", "causal", "mask", "causal+mask"])
+def test_splitkv_matches_oracle(dev, d, mode):
+    """Split-key forward (partials per key range, log-sum-exp merge) against the oracle, for
+    split counts below, at and above the number of 128-key blocks."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    causal = "causal" in mode
+    for N, splits in ((1, 1), (127, 3), (300, 2), (300, 5), (1000, 3), (1000, 8)):
+        t = workloads.random_case(1, 2, N, d, "bf16", seed=1200 + N + splits,
+                                  mask_density=0.6 if "mask" in mode else None, mask_seed=1300 + N)
+        if t.block_mask is not None:
+            np.fill_diagonal(t.block_mask, 1)
+        G.say(f"[case] splitkv N={N} d={d} {mode} splits={splits}")
+        q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+        mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
+        nan = lambda shape, dt: torch.full(shape, float("nan"), dtype=dt, device=dev)
+        o, lse = fa.fwd_splitkv(q, k, v, 1.0 / math.sqrt(d), causal, mask, splits,
+                                out=nan(q.shape, q.dtype), lse=nan(q.shape[:3], torch.float32))
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
+        G.compare_heads(t, {"o": o, "lse": lse}, 1.0 / math.sqrt(d), causal, heads=[(0, 0), (0, 1)], backward=False)
+
+
+def test_splitkv_long_head_sampled(dev):
+    """Few heads and a long causal sequence (the case the split-key form is for): B=1, H=2,
+    N=16384, d=128 with 8 key ranges, sampled rows against the oracle."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    N = 16384
+    t = workloads.random_case(1, 2, N, 128, "bf16", seed=1400, with_do=False)
+    q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+    o, lse = fa.fwd_splitkv(q, k, v, 1.0 / math.sqrt(128), True, None, 8)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(N, 40, seed=1401)
+    G.compare_heads(t, {"o": o, "lse": lse}, 1.0 / math.sqrt(128), True, heads=[(0, 0), (0, 1)], backward=False,
+                    rows=rows)
+
+
+def test_merge_of_oracle_partials(dev):
+    """The merge kernel alone: partial results of the oracle over disjoint key ranges (one of them
+    empty, so every row has a dead part) combine into the oracle's attention over all keys."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+    import oracle
+
+    N, d = 200, 64
+    t = workloads.random_case(1, 1, N, d, "bf16", seed=1500, with_do=False)
+    q, k, v = (G._head(t, x, 0, 0) for x in ("q", "k", "v"))
+    cuts = [(0, 37), (37, 150), (150, 150), (150, 200)]
+    o_parts, l_parts = [], []
+    for lo, hi in cuts:
+        if hi > lo:
+            O, L = oracle.forward_head(q, k[lo:hi], v[lo:hi], 0.125, False, None)
+        else:
+            O, L = np.zeros((N, d)), np.full(N, -np.inf)
+        o_parts.append(O)
+        l_parts.append(L)
+    op = torch.from_numpy(np.stack(o_parts).astype(np.float32)).to(dev)
+    lp = torch.from_numpy(np.stack(l_parts).astype(np.float32)).to(dev)
+    o, lse = fa.merge(op, lp)
+    torch.cuda.synchronize()
+    O, L = oracle.forward_head(q, k, v, 0.125, False, None)
+    G.check("merge O", G.host_f64(o), O, G.TOL_BF16, True)
+    G.check_lse("merge LSE", lse.cpu().numpy(), L)
+    # all parts dead: O = 0, LSE = -inf
+    o2, lse2 = fa.merge(torch.zeros_like(op), torch.full_like(lp, float("-inf")))
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 0) and torch.all(torch.isneginf(lse2))
