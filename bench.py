@@ -7,6 +7,9 @@ resident in device memory.  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
                     [--copy-calibration MIB]
     python bench.py --traffic-from FETCH_CSV WRITE_CSV [--workload long]
+    python bench.py --linear-sweep [--copy-calibration 256]     (under rocprofv3 --pmc)
+    python bench.py --sweep-from FETCH_CSV WRITE_CSV
+    python bench.py --mfma-from COUNTER_CSV
 
 HBM traffic: run the bench twice under `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` with
 `--copy-calibration 256`, which first copies 256 MiB with the runtime's copy kernel.  The two
@@ -121,6 +124,91 @@ def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_mib: int = 
     return head + "\n".join(lines)
 
 
+LINEAR_NS = (4096, 8192, 16384, 32768, 65536)
+
+
+def linear_sweep(dev):
+    """Causal forward at B=1, H=8, d=128 for each N in LINEAR_NS (seeded device-side Gaussian
+    inputs), two calls each; for a counter run that shows how HBM bytes per call grow with N."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    for N in LINEAR_NS:
+        g = torch.Generator(device=dev)
+        g.manual_seed(N)
+        q, k, v = (torch.randn(1, 8, N, 128, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 8, N), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            fa.fwd(q, k, v, 1.0 / 128 ** 0.5, True, None, out=o, lse=lse)
+        torch.cuda.synchronize()
+        print(f"# linear sweep N={N} done", file=sys.stderr, flush=True)
+        del q, k, v, o, lse
+
+
+def sweep_from(fetch_csv: str, write_csv: str, copy_mib: int = 256) -> str:
+    """Markdown table of forward HBM bytes per call against N from two counter files of a
+    --linear-sweep run (the forward grid, N/128 * 8 workgroups, identifies N)."""
+    import statistics
+
+    factors, per_n = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        import csv
+
+        rows = list(csv.DictReader(open(path)))
+        vals, grids = {}, {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            dsp = int(r["Dispatch_Id"])
+            vals[dsp] = vals.get(dsp, 0.0) + float(r["Counter_Value"])
+            grids[dsp] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        copies = [vals[d_] for d_, (n, _) in grids.items() if COPY_KERNEL in n]
+        factors[counter] = copy_mib * 2 ** 20 / (statistics.median(copies) * 1024.0)
+        for d_, (n, grid) in grids.items():
+            if "fwd_bf16_kernel" in n:
+                N = grid // 256 // 8 * 128
+                per_n.setdefault(N, {}).setdefault(counter, []).append(vals[d_] * 1024.0 * factors[counter])
+    lines = [f"FETCH_SIZE factor {factors['FETCH_SIZE']:.3f}, WRITE_SIZE factor {factors['WRITE_SIZE']:.3f} "
+             f"(from the {copy_mib} MiB copy)\n",
+             "| N | algorithmic bytes (Q, K, V read; O, LSE written) | measured HBM bytes/call | measured ÷ algorithmic | "
+             "S+P materialisation (16·N²·H bytes) |", "|---|---|---|---|---|"]
+    for N in sorted(per_n):
+        meas = statistics.median(per_n[N]["FETCH_SIZE"]) + statistics.median(per_n[N]["WRITE_SIZE"])
+        alg = 8 * (4 * N * 128 * 2 + 4 * N)
+        lines.append(f"| {N} | {alg / 1e6:.1f} MB | {meas / 1e6:.1f} MB | {meas / alg:.2f} | {16 * N * N * 8 / 1e9:.1f} GB |")
+    return "\n".join(lines)
+
+
+def mfma_from(csv_path: str) -> str:
+    """Markdown table of MFMA utilisation per attention kernel from a counter run with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE (summed over the 8 XCDs)."""
+    import csv
+    import statistics
+
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        dsp = int(r["Dispatch_Id"])
+        e = per.setdefault(dsp, {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for e in per.values():
+        for key, short in KERNEL_KEYS.items():
+            if key in e["name"] and "SQ_VALU_MFMA_BUSY_CYCLES" in e:
+                cycles = e["GRBM_GUI_ACTIVE"] / 8.0  # per XCD
+                util = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * cycles) if cycles else 0.0
+                out.setdefault(short, []).append((util, cycles / (e["ns"] * 1e-9) / 1e9, e.get("SQ_INSTS_MFMA", 0.0)))
+    lines = ["| kernel | dispatches | MFMA busy ÷ (1024 SIMDs × kernel cycles) | kernel clock from GRBM_GUI_ACTIVE ÷ duration | "
+             "MFMA instructions |", "|---|---|---|---|---|"]
+    for short, v in out.items():
+        u = statistics.median(x[0] for x in v)
+        c = statistics.median(x[1] for x in v)
+        n = statistics.median(x[2] for x in v)
+        lines.append(f"| {short} | {len(v)} | {100 * u:.1f}% | {c:.2f} GHz | {n:.4g} |")
+    return "\n".join(lines)
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the current
     kernel sources; else None."""
@@ -193,9 +281,21 @@ def main():
                     help="copy MIB MiB with the runtime's copy kernel before the bench (counter scaling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter files and exit")
+    ap.add_argument("--linear-sweep", action="store_true",
+                    help="run the causal forward at B=1 H=8 d=128 for N = 4k .. 64k (for a counter run) and exit")
+    ap.add_argument("--sweep-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM bytes per forward call against N from a --linear-sweep counter run and exit")
+    ap.add_argument("--mfma-from", metavar="CSV",
+                    help="print MFMA utilisation per kernel from an SQ counter run and exit")
     args = ap.parse_args()
     if args.traffic_from:
         print(traffic_from(*args.traffic_from, workload=args.workload, copy_mib=args.copy_calibration or 256))
+        return
+    if args.sweep_from:
+        print(sweep_from(*args.sweep_from, copy_mib=args.copy_calibration or 256))
+        return
+    if args.mfma_from:
+        print(mfma_from(args.mfma_from))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -219,6 +319,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.linear_sweep:
+        linear_sweep(dev)
+        return
     t_gen = time.perf_counter()
     t = workloads.make(w, with_do=not w.fwd_only)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
