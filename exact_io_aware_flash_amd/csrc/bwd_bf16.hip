@@ -212,7 +212,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
       }
     }
     // dV += P^T dO ; dK += dS^T Q (contraction over the 32 queries, two chunks of 16); each MFMA
-    // takes one transposed B operand (two 8-byte transposing reads), kept two MFMAs ahead
+    // takes one transposed B operand (two 8-byte transposing reads), kept four MFMAs ahead (one
+    // wave per SIMD: nothing else hides the read latency)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -223,13 +224,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
         dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
                            dkacc[db]);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-    for (int i = 0; i < 4 * DB - 2; ++i) {
+    for (int i = 0; i < 4 * DB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
   auto step = [&](int t, auto parity) {

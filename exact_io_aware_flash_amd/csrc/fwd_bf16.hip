@@ -202,7 +202,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
 
     // next tile's scores: independent of the exponentials below, so the two can overlap
     f32x16 s_nxt[2];
+    // MFMA sections run at raised wave priority, so that when both waves of a SIMD can issue,
+    // the one feeding the matrix pipe goes first and the other's softmax fills the gaps
+    __builtin_amdgcn_s_setprio(1);
     if (has1) scores(k_next, s_nxt);
+    __builtin_amdgcn_s_setprio(0);
 
     // P in fp32 feeds the row sum (so LSE carries fp32 error only); its bf16 rounding feeds PV.
     // pk[2 kb + m2] holds keys k0 + 32 kb + 16 m2 + 8h + 0..7: one k-slot group of the PV MFMA.
@@ -220,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
         }
     lsum += (part[0] + part[1]) + (part[2] + part[3]);
 
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T over the 64 keys (4 contraction chunks of 16; V^T read transposed)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -237,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 
+    __builtin_amdgcn_s_setprio(0);
     wait_dma();
     __syncthreads();
     if (has1) {
