@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
 // ------------------------------------------------------------------------------------- dK, dV
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
-  constexpr int BKV = 128, BQ = 64;
+  constexpr int BKV = 128, BQ = 128;  // one mask block of keys against one of queries per step
+  constexpr int NH = BQ / 32;          // 32-query parts of a query tile
   constexpr int DC = D / 16, DB = D / 32;
   using QT = DmaTile<BQ, D>;  // Q or dO rows (read row-wise and transposed)
 
@@ -93,11 +94,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     }
     __syncthreads();
     const int cnt = bcount;
-    ntiles = 2 * cnt;
-    if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BQ >= N) ntiles -= 1;
+    ntiles = cnt;  // one query tile per mask block
   }
   auto tile_start = [&](int t) -> int {
-    if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BQ;
+    if (SPARSE) return (int)blist[t] * kMaskBlock;
     return (q_first + t) * BQ;
   };
 
@@ -252,11 +252,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     // (d = 64 runs one body for every tile: a second copy costs it its second wave per SIMD)
     const bool tile_mask = (D == 64) || (k0 + BKV > N) || (CAUSAL && q0 < k0 + BKV - 1);
     if (!tile_mask) {
-      half(std::false_type{}, tq, to, Ls, Ds, 0, q0);
-      half(std::false_type{}, tq, to, Ls, Ds, 1, q0 + 32);
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        half(std::false_type{}, tq, to, Ls, Ds, s, q0 + 32 * s);
+        // keep the parts apart: hoisting the next part's operand reads over this one only
+        // raises register pressure (one wave per SIMD hides nothing with it)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < NH; ++s) {
         const int qs = q0 + 32 * s;
         if (qs >= N) continue;
         if (CAUSAL && qs + 31 < k0w) continue;  // every query of this half precedes every key of the wave
