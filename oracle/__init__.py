@@ -10,6 +10,8 @@ Contents
                 definition; row-chunked so that long sequences fit host memory.
   online.py     the pages' tiled loop with the online-softmax update, in fp64, used by the
                 tests as an independent witness that the re-association is exact.
+  mx.py         MX-FP8 (E4M3 elements, power-of-two scales per 32 elements) quantisation from
+                the OCP Microscaling Formats specification, for the FP8 forward's inputs.
 
 Page keys used in citations:
   [P1] "How FlashAttention Bypasses the GPU Memory Bottleneck to Enable Long-Context AI" (factlen.com)
@@ -18,7 +20,9 @@ Page keys used in citations:
 
 Parity status: every function here is pinned by `tests/test_oracle.py` (brute force on tiny
 inputs, closed forms, invariants of softmax attention, central finite differences for the
-backward, and agreement with the tiled online-softmax loop).  No function is parity-unpinned.
+backward, and agreement with the tiled online-softmax loop) and `tests/test_oracle_mx.py` (the
+E4M3 code table, nearest-even rounding by brute force over every code, the shared-exponent
+rule).  No function is parity-unpinned.
 """
 from .attention import (  # noqa: F401
     MASK_BLOCK,
@@ -31,3 +35,4 @@ from .attention import (  # noqa: F401
     s_matrix_bytes,
 )
 from .online import tiled_forward_head  # noqa: F401
+from . import mx  # noqa: F401
