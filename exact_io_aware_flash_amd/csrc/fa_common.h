@@ -264,9 +264,13 @@ struct TransStage {
 // v_permlane32_swap exchanges the upper half of its first operand with the lower half of its
 // second; called with (x, x) every lane ends up holding both its own value and its partner's.
 // ---------------------------------------------------------------------------------------------
+// maximum that propagates NaN (IEEE maximum): unlike fmaxf it needs no canonicalising moves of
+// its operands, and three of them fuse into one v_maximum3_f32
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

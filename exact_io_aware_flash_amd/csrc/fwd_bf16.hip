@@ -52,7 +52,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int bcount;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+  // the wave index is uniform: held in a scalar register, the LDS targets of the copies need no
+  // per-issue v_readfirstlane
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+            c32 = lane & 31;
   const int N = a.N;
   int bh, qt;
   sched_decode(sc, gridDim.x, bh, qt);
@@ -149,8 +152,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   //   iteration t:  copies of K[t+2], V[t+1] in flight;  softmax of S[t] next to the MFMAs of
   //                 S[t+1] = K[t+1] Q^T;  O += V[t] P[t];  wait for the copies; barrier.
   // K tiles alternate between kbuf0/kbuf1 and V tiles between vbuf0/vbuf1, so the buffer a copy
-  // lands in during iteration t is never one read in iteration t.
-  f32x16 s_cur[2];
+  // lands in during iteration t is never one read in iteration t.  The scores alternate between
+  // sbuf[0] and sbuf[1] the same way, so no step copies registers.
+  f32x16 sbuf[2][2];
   if (ntiles > 0) {
     kdma.issue(K, N, kbuf0, tile_start(0), w);
     vdma.issue(V, N, vbuf0, tile_start(0), w);
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   }
   wait_dma();
   __syncthreads();
-  if (ntiles > 0) scores(kbuf0, s_cur);
+  if (ntiles > 0) scores(kbuf0, sbuf[0]);
 
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;  // t % 2
@@ -166,6 +170,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     char* const k_free = par ? kbuf1 : kbuf0;      // held K[t]; receives K[t+2]
     char* const v_cur = par ? vbuf1 : vbuf0;       // holds V[t]
     char* const v_free = par ? vbuf0 : vbuf1;      // held V[t-1]; receives V[t+1]
+    f32x16(&s_cur)[2] = sbuf[par];
+    f32x16(&s_nxt)[2] = sbuf[par ^ 1];
     const int k0 = tile_start(t);
     const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles;
     if (has2) kdma.issue(K, N, k_free, tile_start(t + 2), w);
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_cur[kb][r]);
+      for (int r = 0; r < 16; ++r) mt = fmax_nan(mt, s_cur[kb][r]);
     mt = half_swap_max(mt) * sl;
     const float m_new = (mt > m_used + kRescaleThreshold) ? mt : m_used;
     const float alpha = (m_new == m_used) ? 1.f : fast_exp2(m_used - m_new);
@@ -200,8 +206,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     }
     const float msub = (m_used == neg_inf()) ? 0.f : m_used;
 
-    // next tile's scores: independent of the exponentials below, so the two can overlap
-    f32x16 s_nxt[2];
+    // next tile's scores: independent of the exponentials below, so the two can overlap.
     // MFMA sections run at raised wave priority, so that when both waves of a SIMD can issue,
     // the one feeding the matrix pipe goes first and the other's softmax fills the gaps
     __builtin_amdgcn_s_setprio(1);
@@ -245,10 +250,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     __builtin_amdgcn_s_setprio(0);
     wait_dma();
     __syncthreads();
-    if (has1) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
-    }
   };
 
   for (int t = 0; t < ntiles; t += 2) {
