@@ -129,9 +129,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   kdma.init(w, lane);
   vdma.init(w, lane);
 
-  // S^T = K Q^T for two 32-key blocks; register r of half h holds key k0 + 32 kb + acc_row(r, h)
-  // the two 32-key blocks alternate, so consecutive MFMAs are independent; K reads run four
-  // MFMAs ahead of their use (the scheduling groups keep the compiler from sinking them)
+  // S^T = K Q^T for two 32-key blocks; register r of half h holds key k0 + 32 kb + acc_row(r, h).
+  // The two 32-key blocks alternate, so consecutive MFMAs are independent.
   auto scores = [&](const char* tk, f32x16(&s)[2]) {
     s[0] = zero16();
     s[1] = zero16();
@@ -139,22 +138,47 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     for (int c = 0; c < DC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(lds_b128(tk + kaddr[c] + 32 * kb * D * 2), qreg[c], s[kb]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  };
+  // element masks: the causal diagonal and the key tail (only tiles that reach either)
+  auto mask_tile = [&](f32x16(&s)[2], int k0) {
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w)) {
 #pragma unroll
-    for (int i = 0; i < 2 * DC - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + acc_row(r, h);
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
+        }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // online softmax: the running max (scaled log2 units) moves only when a score exceeds it by
+  // more than 2^8; alpha is the factor that moves the accumulated O and sum onto the new max
+  auto update_max = [&](const f32x16(&s)[2], float& m, float& alpha) {
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmax_nan(mt, s[kb][r]);
+    mt = half_swap_max(mt) * sl;
+    const float m_new = (mt > m + kRescaleThreshold) ? mt : m;
+    alpha = (m_new == m) ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
   };
 
-  // Software pipeline over key tiles (K runs one tile ahead of V):
-  //   iteration t:  copies of K[t+2], V[t+1] in flight;  softmax of S[t] next to the MFMAs of
-  //                 S[t+1] = K[t+1] Q^T;  O += V[t] P[t];  wait for the copies; barrier.
-  // K tiles alternate between kbuf0/kbuf1 and V tiles between vbuf0/vbuf1, so the buffer a copy
-  // lands in during iteration t is never one read in iteration t.  The scores alternate between
-  // sbuf[0] and sbuf[1] the same way, so no step copies registers.
+  // Software pipeline over key tiles (K runs one tile ahead of V, the scores and the max one
+  // tile ahead of the exponentials):
+  //   iteration t:  copies of K[t+2], V[t+1] in flight;
+  //                 section 1: MFMAs of S[t+1] = K[t+1] Q^T, the exponentials of S[t] between them;
+  //                 section 2: MFMAs of O += V[t] P[t], the row sums of P[t] and the max of S[t+1]
+  //                            between them;  wait for the copies; barrier.
+  // Each section pairs one matrix chain with VALU work that does not feed it, so the SIMD can
+  // issue both.  K tiles alternate between kbuf0/kbuf1 and V tiles between vbuf0/vbuf1, so the
+  // buffer a copy lands in during iteration t is never one read in iteration t.  The scores
+  // alternate between sbuf[0] and sbuf[1] the same way, so no step copies registers.  The last
+  // tile's section 1 multiplies the stale K buffer (in bounds; the result is discarded), which
+  // keeps every section free of branches.
   f32x16 sbuf[2][2];
+  float alpha = 1.f;
   if (ntiles > 0) {
     kdma.issue(K, N, kbuf0, tile_start(0), w);
     vdma.issue(V, N, vbuf0, tile_start(0), w);
@@ -162,43 +186,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   }
   wait_dma();
   __syncthreads();
-  if (ntiles > 0) scores(kbuf0, sbuf[0]);
+  if (ntiles > 0) {
+    scores(kbuf0, sbuf[0]);
+    mask_tile(sbuf[0], tile_start(0));
+    update_max(sbuf[0], m_used, alpha);
+    alpha = 1.f;  // nothing accumulated yet
+  }
 
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;  // t % 2
-    char* const k_next = par ? kbuf0 : kbuf1;      // holds K[t+1]
+    char* const k_next = par ? kbuf0 : kbuf1;      // holds K[t+1] (stale K on the last tile)
     char* const k_free = par ? kbuf1 : kbuf0;      // held K[t]; receives K[t+2]
     char* const v_cur = par ? vbuf1 : vbuf0;       // holds V[t]
     char* const v_free = par ? vbuf0 : vbuf1;      // held V[t-1]; receives V[t+1]
     f32x16(&s_cur)[2] = sbuf[par];
     f32x16(&s_nxt)[2] = sbuf[par ^ 1];
-    const int k0 = tile_start(t);
     const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles;
     if (has2) kdma.issue(K, N, k_free, tile_start(t + 2), w);
     if (has1) vdma.issue(V, N, v_free, tile_start(t + 1), w);
 
-    // element masks: the causal diagonal and the key tail
-    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + acc_row(r, h);
-          if (key >= N || (CAUSAL && key > qrow)) s_cur[kb][r] = neg_inf();
-        }
-    }
-
-    // online softmax: running max moves only when a score exceeds it by more than 2^8
-    float mt = s_cur[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmax_nan(mt, s_cur[kb][r]);
-    mt = half_swap_max(mt) * sl;
-    const float m_new = (mt > m_used + kRescaleThreshold) ? mt : m_used;
-    const float alpha = (m_new == m_used) ? 1.f : fast_exp2(m_used - m_new);
-    m_used = m_new;
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
@@ -206,31 +212,55 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     }
     const float msub = (m_used == neg_inf()) ? 0.f : m_used;
 
-    // next tile's scores: independent of the exponentials below, so the two can overlap.
-    // MFMA sections run at raised wave priority, so that when both waves of a SIMD can issue,
-    // the one feeding the matrix pipe goes first and the other's softmax fills the gaps
-    __builtin_amdgcn_s_setprio(1);
-    if (has1) scores(k_next, s_nxt);
-    __builtin_amdgcn_s_setprio(0);
-
-    // P in fp32 feeds the row sum (so LSE carries fp32 error only); its bf16 rounding feeds PV.
+    // section 1: S[t+1], and P[t] = exp2(S[t] * scale * log2(e) - m) in fp32 (kept in s_cur for
+    // the row sum, so LSE carries fp32 error only) and rounded to bf16 for PV.
     // pk[2 kb + m2] holds keys k0 + 32 kb + 16 m2 + 8h + 0..7: one k-slot group of the PV MFMA.
+    // Written out slot by slot in issue order (fenced, so the compiler keeps it): each MFMA is
+    // followed by the FMAs of the next slot's scores, the exponentials of this slot's and the
+    // bf16 conversion of the previous slot's; K operands are read four MFMAs ahead.
+    constexpr int NS = 2 * DC;    // MFMAs (slots) in the section
+    constexpr int EPS = 32 / NS;  // exponentials per slot
+    auto sc = [&](int j) -> float { return s_cur[j >> 4][j & 15]; };
+    auto kread = [&](int i) { return lds_b128(k_next + kaddr[i >> 1] + 32 * (i & 1) * D * 2); };
     bf16x8 pk[4];
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8 kop[NS];
+      float y[32];
+      s_nxt[0] = zero16();
+      s_nxt[1] = zero16();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 4; ++i) kop[i] = kread(i);
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
+      for (int j = 0; j < EPS; ++j) y[j] = __builtin_fmaf(sc(j), sl, -msub);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(__builtin_fmaf(s_cur[kb][8 * m2 + e], sl, -msub));
-          part[e & 3] += pv;
-          pk[2 * kb + m2][e] = (__bf16)pv;
+      for (int i = 0; i < NS; ++i) {
+        if (i + 4 < NS) kop[i + 4] = kread(i + 4);
+        s_nxt[i & 1] = mfma32(kop[i], qreg[i >> 1], s_nxt[i & 1]);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e)
+          if ((i + 1) * EPS + e < 32) y[(i + 1) * EPS + e] = __builtin_fmaf(sc((i + 1) * EPS + e), sl, -msub);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) s_cur[(i * EPS + e) >> 4][(i * EPS + e) & 15] = fast_exp2(y[i * EPS + e]);
+        if (i > 0) {
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) pk[((i - 1) * EPS + e) >> 3][((i - 1) * EPS + e) & 7] = (__bf16)sc((i - 1) * EPS + e);
         }
-    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) pk[((NS - 1) * EPS + e) >> 3][((NS - 1) * EPS + e) & 7] = (__bf16)sc((NS - 1) * EPS + e);
+    }
+    // pin P[t] here: without a use in this section the compiler sinks the exponentials past the
+    // mask branch below, away from the MFMAs they are meant to run beside
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pk[i]));
+    asm volatile("" : "+v"(s_cur[0]), "+v"(s_cur[1]));
+    __builtin_amdgcn_sched_barrier(0);
 
-    __builtin_amdgcn_s_setprio(1);
-    // O^T += V^T P^T over the 64 keys (4 contraction chunks of 16; V^T read transposed)
+    if (has1) mask_tile(s_nxt, tile_start(t + 1));
+
+    // section 2: O^T += V^T P^T over the 64 keys (4 contraction chunks of 16; V^T read
+    // transposed), the row sum of P[t] and the running max after S[t+1]
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -238,16 +268,29 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
         const char* vb = v_cur + 16 * m * D * 2;
         oacc[db] = mfma32(join8(lds_tr4(vb + vaddr[0][db]), lds_tr4(vb + vaddr[1][db])), pk[m], oacc[db]);
       }
-    // each PV MFMA takes one transposed operand (two 8-byte reads), kept two MFMAs ahead
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[r & 3] += s_cur[kb][r];
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+    asm volatile("" : "+v"(lsum));  // keep the row sums in this section as well
+    {
+      float m_nx = m_used, a_nx;
+      update_max(s_nxt, m_nx, a_nx);
+      asm volatile("" : "+v"(m_nx), "+v"(a_nx));  // computed here, whether or not used
+      m_used = has1 ? m_nx : m_used;
+      alpha = has1 ? a_nx : alpha;
+    }
+    // per MFMA: one transposed operand (two 8-byte reads, two MFMAs ahead), VALU work between
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-    for (int i = 0; i < 4 * DB - 2; ++i) {
+    for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      if (i < 4 * DB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     wait_dma();
     __syncthreads();
   };
