@@ -70,6 +70,14 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_fwd_splitkv.restype = i
     L.flash_attn_merge.argtypes = [vp, vp, i, ctypes.c_int64, i, vp, vp, vp]
     L.flash_attn_merge.restype = i
+    L.flash_attn_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_fwd_mxfp8.restype = i
+    L.flash_attn_mxfp8_quantize_rows.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.flash_attn_mxfp8_quantize_rows.restype = i
+    L.flash_attn_mxfp8_quantize_vt.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.flash_attn_mxfp8_quantize_vt.restype = i
+    L.flash_attn_mxfp8_vt_cols.argtypes = [i]
+    L.flash_attn_mxfp8_vt_cols.restype = ctypes.c_int64
     L.flash_attn_status_string.argtypes = [i]
     L.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -327,6 +335,75 @@ def bwd_dq(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=Non
 # keeps O and LSE for the backward, which recomputes S and P tile by tile from them (the
 # recomputation of the backward pass: "How FlashAttention Eliminates Transformer Memory
 # Bottlenecks", Innovation #3).  Both directions run in the library's kernels.
+class MXFP8:
+    """An MX-FP8 tensor as the FP8 forward reads it: E4M3 codes (uint8) and E8M0 block scales
+    (uint8, value 2^(s - 127)).  `transposed` marks V's feature-major layout."""
+
+    def __init__(self, codes, scales, transposed: bool, shape):
+        self.codes, self.scales, self.transposed, self.shape = codes, scales, transposed, tuple(shape)
+
+
+def mxfp8_vt_cols(N: int) -> int:
+    return int(lib().flash_attn_mxfp8_vt_cols(N))
+
+
+def mxfp8_quantize(x, transposed: bool = False, stream=None) -> MXFP8:
+    """MX-FP8 quantisation of a bf16 [B, H, N, d] CUDA tensor: blocks of 32 along d (Q, K), or
+    with transposed=True blocks of 32 keys into V's transposed layout [B, H, d, Np]."""
+    import torch
+
+    B, H, N, d = x.shape
+    _check(x, "x", torch.bfloat16, (B, H, N, d), x.device)
+    L = lib()
+    if transposed:
+        npad = mxfp8_vt_cols(N)
+        codes = torch.empty((B, H, d, npad), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((B, H, npad // 32, 32, d // 32), dtype=torch.uint8, device=x.device)
+        st = L.flash_attn_mxfp8_quantize_vt(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, _stream(stream))
+        where = "flash_attn_mxfp8_quantize_vt"
+    else:
+        codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
+        st = L.flash_attn_mxfp8_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, _stream(stream))
+        where = "flash_attn_mxfp8_quantize_rows"
+    if st != FA_OK:
+        raise FlashAttnError(st, where)
+    return MXFP8(codes, scales, transposed, (B, H, N, d))
+
+
+def fwd_mxfp8(q: MXFP8, k: MXFP8, vt: MXFP8, scale: float | None = None, causal: bool = False, block_mask=None,
+              out=None, lse=None, stream=None):
+    """MX-FP8 forward from quantised Q, K (row blocks) and V (transposed).  Returns
+    (o [B, H, N, d] bf16, lse [B, H, N] float32)."""
+    import torch
+
+    B, H, N, d = q.shape
+    if k.shape != q.shape or vt.shape != q.shape or q.transposed or k.transposed or not vt.transposed:
+        raise ValueError("fwd_mxfp8: q, k row-quantised and vt transposed, all of one [B, H, N, d] shape")
+    dev = q.codes.device
+    npad = mxfp8_vt_cols(N)
+    _check(q.codes, "q.codes", torch.uint8, (B, H, N, d), dev)
+    _check(k.codes, "k.codes", torch.uint8, (B, H, N, d), dev)
+    _check(q.scales, "q.scales", torch.uint8, (B, H, N, d // 32), dev)
+    _check(k.scales, "k.scales", torch.uint8, (B, H, N, d // 32), dev)
+    _check(vt.codes, "vt.codes", torch.uint8, (B, H, d, npad), dev)
+    _check(vt.scales, "vt.scales", torch.uint8, (B, H, npad // 32, 32, d // 32), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_fwd_mxfp8(_ptr(q.codes), _ptr(q.scales), _ptr(k.codes), _ptr(k.scales), _ptr(vt.codes),
+                                    _ptr(vt.scales), _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
+                                    _ptr(bm), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_mxfp8")
+    return out, lse
+
+
 def _attention_fn():
     import torch
 

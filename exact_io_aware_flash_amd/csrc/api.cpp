@@ -252,6 +252,77 @@ int flash_attn_merge(const float* o_parts, const float* lse_parts, int parts, in
   return status_of(fa::launch_merge_bf16(o_parts, lse_parts, parts, rows, d, static_cast<__bf16*>(o), lse, stream));
 }
 
+int64_t flash_attn_mxfp8_vt_cols(int N) { return N < 1 ? 0 : (int64_t)fa::fp8_vt_cols(N); }
+
+int flash_attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* q_scales, const uint8_t* k8, const uint8_t* k_scales,
+                         const uint8_t* vt8, const uint8_t* vt_scales, void* o, float* lse, int B, int H, int N, int d,
+                         float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  if (!q8 || !q_scales || !k8 || !k_scales || !vt8 || !vt_scales || !o || !lse) return FA_ERR_NULL;
+  long long elems = 0;
+  int st = check_common(B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q8, q_scales, k8, k_scales, vt8, vt_scales, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const long long bh = (long long)B * H, np = fa::fp8_vt_cols(N);
+  const long long cb = elems, sb = elems / 32, vtb = bh * d * np, vsb = bh * np * (d / 32);
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[7] = {rng(q8, cb),  rng(q_scales, sb),  rng(k8, cb), rng(k_scales, sb),
+                 rng(vt8, vtb), rng(vt_scales, vsb), rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[2] = {rng(o, elems * 2), rng(lse, bh * N * 4)};
+  st = check_alias(in, 7, out, 2);
+  if (st != FA_OK) return st;
+  fa::Fp8FwdArgs a = {};
+  a.q8 = q8;
+  a.qs = q_scales;
+  a.k8 = k8;
+  a.ks = k_scales;
+  a.vt8 = vt8;
+  a.vts = vt_scales;
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.mask = block_mask;
+  a.N = N;
+  a.Np = (int)np;
+  a.d = d;
+  a.BH = (int)bh;
+  a.nb = (int)nb;
+  a.causal = causal;
+  a.scale_log2 = scale * fa::kLog2e;
+  return status_of(fa::launch_fwd_mxfp8(a, stream));
+}
+
+int flash_attn_mxfp8_quantize_rows(const void* x, uint8_t* codes, uint8_t* scales, int B, int H, int N, int d,
+                                   hipStream_t stream) {
+  if (!x || !codes || !scales) return FA_ERR_NULL;
+  long long elems = 0;
+  int st = check_common(B, H, N, d, 1.0f, 0, nullptr, true, &elems);
+  if (st != FA_OK) return st;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FA_ERR_ALIGN;
+  Range in[1] = {rng(x, elems * 2)};
+  Range out[2] = {rng(codes, elems), rng(scales, elems / 32)};
+  st = check_alias(in, 1, out, 2);
+  if (st != FA_OK) return st;
+  return status_of(
+      fa::launch_mxfp8_quantize_rows(static_cast<const __bf16*>(x), codes, scales, (long long)B * H * N, d, stream));
+}
+
+int flash_attn_mxfp8_quantize_vt(const void* v, uint8_t* codes_t, uint8_t* scales_t, int B, int H, int N, int d,
+                                 hipStream_t stream) {
+  if (!v || !codes_t || !scales_t) return FA_ERR_NULL;
+  long long elems = 0;
+  int st = check_common(B, H, N, d, 1.0f, 0, nullptr, true, &elems);
+  if (st != FA_OK) return st;
+  if ((long long)B * H > 65535) return FA_ERR_SHAPE;  // heads on grid.y
+  if (!aligned16(v) || !aligned16(codes_t) || !aligned16(scales_t)) return FA_ERR_ALIGN;
+  const long long bh = (long long)B * H, np = fa::fp8_vt_cols(N);
+  Range in[1] = {rng(v, elems * 2)};
+  Range out[2] = {rng(codes_t, bh * d * np), rng(scales_t, bh * np * (d / 32))};
+  st = check_alias(in, 1, out, 2);
+  if (st != FA_OK) return st;
+  return status_of(fa::launch_mxfp8_quantize_vt(static_cast<const __bf16*>(v), codes_t, scales_t, (int)bh, N, d, stream));
+}
+
 int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                        int d, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
   long long elems = 0;

@@ -101,7 +101,32 @@ inline Sched make_sched(int ntiles, int BH, int heavy_last_tile, int slots_per_x
   return s;
 }
 
+// MX-FP8 forward: E4M3 element codes with one E8M0 scale per block of 32.  Q and K are
+// row-quantised ([BH, N, d] codes, [BH, N, d/32] scales, blocks along d); V is stored transposed
+// ([BH, d, Np] codes, keys >= N zero, Np = N rounded up to 64) with blocks of 32 keys, scale of
+// (feature f, key block j) at ((bh * Np/32 + j) * 32 + f % 32) * (d/32) + f / 32.
+struct Fp8FwdArgs {
+  const uint8_t* q8;
+  const uint8_t* qs;
+  const uint8_t* k8;
+  const uint8_t* ks;
+  const uint8_t* vt8;
+  const uint8_t* vts;
+  __bf16* o;
+  float* lse;
+  const uint8_t* mask;
+  int N, Np, d, BH, nb, causal;
+  float scale_log2;
+};
+inline int fp8_vt_cols(int N) { return (N + 63) / 64 * 64; }
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_mxfp8(const Fp8FwdArgs& a, hipStream_t stream);
+// MX-FP8 quantisation of bf16 rows (blocks of 32 along d), and of V into the transposed layout
+hipError_t launch_mxfp8_quantize_rows(const __bf16* x, uint8_t* codes, uint8_t* scales, long long rows, int d,
+                                      hipStream_t stream);
+hipError_t launch_mxfp8_quantize_vt(const __bf16* v, uint8_t* codes_t, uint8_t* scales_t, int BH, int N, int d,
+                                    hipStream_t stream);
 // split-key forward: partials into a.o_part / a.lse_part, then the log-sum-exp merge into a.o / a.lse
 hipError_t launch_fwd_splitkv_bf16(const FwdArgs& a, hipStream_t stream);
 // log-sum-exp merge of `parts` partial results over disjoint key sets of the same `rows` rows

@@ -1,0 +1,537 @@
+// MX-FP8 forward pass for gfx950: E4M3 operands with power-of-two block scales on the scaled
+// matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), fp32 accumulation and softmax.
+//
+// Method: the same tiled forward with online softmax as the bf16 kernel ([P2] "FlashAttention:
+// how a memory trick unlocked today's giant AI models", "Tiling: Breaking the Problem into
+// Pieces" and "The Trick: Online Softmax"); FP8 arithmetic is the variant [P1] "How
+// FlashAttention Bypasses the GPU Memory Bottleneck to Enable Long-Context AI" names for
+// FlashAttention-3 (about 1.2 PFLOP/s on H100).  The pages fix no FP8 format; the one used is
+// OCP MXFP8 (E4M3 elements, one E8M0 scale per 32 consecutive elements of the contraction
+// index), the block-scaled format these matrix cores multiply natively.
+//
+// Inputs arrive quantised (the two quantisation kernels below, or any producer of the same
+// layout): Q and K in blocks of 32 features, V transposed (feature-major) in blocks of 32 keys,
+// so that both contractions (QK^T over features, PV over keys) see their block scales along
+// the contraction index.  P is quantised in the kernel with scale 1 (P <= 2^8 < 448 under the
+// lazy rescale below); the row sums use P in fp32, so LSE carries fp32 error only.
+//
+// Scaled MFMA operand layout (32 x 32 x 64, E4M3): lane l = 32 h + c holds row (A) or column
+// (B) c; its byte j is contraction index k = 32 (j / 16) + 16 h + j % 16; its scale byte
+// applies to row/column c and k-block h (k = 32 h .. 32 h + 31).  The output is the usual
+// 32 x 32 fp32 layout (register r of lane l: row 8 (r / 4) + 4 h + r % 4, column c).
+//
+//  * S^T = K Q^T: A = K rows from LDS, B = Q (registers for the whole kernel).  A-row i loads
+//    key pi(i) = 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3) of its 32-key block, which puts key
+//    16 h + r of the block in register r of lane half h: exactly the key of byte 16 kb + r of
+//    the lane's P operand below.  So P^T = exp(S^T) feeds the PV MFMA from the lane's own
+//    registers.
+//  * O^T += V^T P^T: A = V^T rows (features) from LDS, B = P^T.
+//  * K / V tiles of 64 keys arrive by asynchronous global->LDS copies, double-buffered, with a
+//    16-byte-chunk XOR swizzle that keeps the 16-byte operand reads free of bank conflicts.
+//  * Same software pipeline as the bf16 kernel: the exponentials of tile t run between the
+//    score MFMAs of tile t+1; the row sums of tile t and the max of tile t+1 between the PV
+//    MFMAs of tile t.
+#include <type_traits>
+
+#include "fa_common.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kRescaleThresholdFp8 = 8.0f;  // log2 units: P <= 2^8 stays below E4M3's 448
+constexpr float kE4M3Max = 448.f;
+constexpr int kP8Scale = 127;  // E8M0 byte of 2^0: P is quantised unscaled
+
+// ---------------------------------------------------------------------------------------------
+// MX-FP8 quantisation of one block of 32 (OCP MX v1.0, section 6.3): shared exponent
+// floor(log2(max |x|)) - 8 (8 = exponent of E4M3's largest normal), held to [-127, 127]; a
+// zero block takes -127.  Elements x * 2^-e, clamped to +-448, rounded to nearest-even E4M3 by
+// v_cvt_pk_fp8_f32 (which does not saturate by itself).  Inputs are finite.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int field = (int)((__float_as_uint(amax) >> 23) & 0xff);  // floor(log2) + 127 for normals
+  return max(-127, min(127, field - 127 - 8));                     // zero / subnormal: -127
+}
+
+__device__ __forceinline__ float mx_scaled(float x, int e) {
+  return fminf(fmaxf(__builtin_ldexpf(x, -e), -kE4M3Max), kE4M3Max);
+}
+
+// codes of four consecutive elements in one dword, first element in the low byte
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, int e) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(a, e), mx_scaled(b, e), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(c, e), mx_scaled(d, e), r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// One thread per block of 32 consecutive elements of x ([rows, d] bf16, d a multiple of 32).
+__global__ __launch_bounds__(256) void mx_quantize_rows_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales, long long nblocks) {
+  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = bf16_lo(w4[j]);
+      v[8 * i + 2 * j + 1] = bf16_hi(w4[j]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_exponent(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], e);
+  uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[b] = (uint8_t)(e + 127);
+}
+
+// V [BH, N, D] bf16 -> V^T codes [BH, D, Np] and scales (blocks of 32 keys).  One workgroup per
+// (head, 64-key chunk): the chunk is staged in LDS (rows >= N as zero), then thread (f, half)
+// quantises the 32 keys 32 half .. 32 half + 31 of feature f.
+template <int D>
+__global__ __launch_bounds__(256) void mx_quantize_vt_kernel(const __bf16* __restrict__ v, uint8_t* __restrict__ codes_t,
+                                                             uint8_t* __restrict__ scales_t, int N, int Np) {
+  constexpr int ROWB = D * 2;  // bytes per staged row
+  __shared__ __attribute__((aligned(16))) char tile[64 * ROWB];
+  const int bh = blockIdx.y, k0 = blockIdx.x * 64, tid = threadIdx.x;
+  const __bf16* head = v + (size_t)bh * N * D;
+  constexpr int CHUNKS = 64 * ROWB / 16;
+  for (int ch = tid; ch < CHUNKS; ch += 256) {
+    const int row = ch / (ROWB / 16), col = ch % (ROWB / 16);
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (k0 + row < N) u = reinterpret_cast<const uint4*>(head + (size_t)(k0 + row) * D)[col];
+    *reinterpret_cast<uint4*>(tile + row * ROWB + col * 16) = u;
+  }
+  __syncthreads();
+  if (tid >= 2 * D) return;
+  const int f = tid % D, half = tid / D;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const unsigned short bits = *reinterpret_cast<const unsigned short*>(tile + (32 * half + i) * ROWB + 2 * f);
+    x[i] = __uint_as_float((uint32_t)bits << 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const int e = mx_exponent(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = mx_pack4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3], e);
+  uint4* dst = reinterpret_cast<uint4*>(codes_t + ((size_t)bh * D + f) * Np + k0 + 32 * half);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  const int kblk = k0 / 32 + half;
+  scales_t[(((size_t)bh * (Np / 32) + kblk) * 32 + f % 32) * (D / 32) + f / 32] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Forward kernel
+// ---------------------------------------------------------------------------------------------
+// E4M3 x E4M3 with block scales: sa / sb hold the scale bytes of this lane's row / column, the
+// byte used picked by OA / OB
+template <int OA, int OB>
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+// the same with both scale bytes chosen by a selector that is a constant after unrolling
+__device__ __forceinline__ f32x16 mfma_mx_sel(int oa, int ob, i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  if (oa == 0 && ob == 0) return mfma_mx<0, 0>(a, b, c, sa, sb);
+  if (oa == 1 && ob == 0) return mfma_mx<1, 0>(a, b, c, sa, sb);
+  if (oa == 2 && ob == 0) return mfma_mx<2, 0>(a, b, c, sa, sb);
+  if (oa == 3 && ob == 0) return mfma_mx<3, 0>(a, b, c, sa, sb);
+  return mfma_mx<2, 2>(a, b, c, sa, sb);
+}
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// K tile: 64 key rows of D bytes; V^T tile: D feature rows of 64 bytes.  Chunk swizzles (16-byte
+// chunks, 256-byte bank window): the 16 lanes of one read pass read one logical chunk of 16
+// rows, so the (row mod rows-per-window, physical chunk) pairs must be distinct.  K rows in a
+// pass are pi(0..15) or pi(16..31) (plus 32 kb): {0..7, 16..23} or {8..15, 24..31}.
+template <int D>
+__device__ __forceinline__ constexpr int sw_k8(int row) {
+  return D >= 128 ? (((row >> 1) & 3) | (((row >> 4) & 1) << 2)) : (((row >> 2) & 1) | (((row >> 4) & 1) << 1));
+}
+__device__ __forceinline__ constexpr int sw_v8(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ constexpr int pi32(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+__device__ __forceinline__ i32x8 join16x2(uint4 a, uint4 b) {
+  i32x8 r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
+}
+__device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched sc) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int DF = D / 64;   // 64-deep contraction chunks over d (score MFMAs per 32-key block)
+  constexpr int DB = D / 32;   // 32-feature output blocks (PV MFMAs per tile)
+  constexpr int NSB = D / 32;  // scale bytes per Q / K row
+  constexpr int KT = BC * D, VT = D * BC;  // tile bytes
+  constexpr int KCH = D / 16;              // 16-byte chunks per K row
+  constexpr int KI = KT / 1024 / 4, VI = VT / 1024 / 4;  // copy instructions per wave and tile
+
+  __shared__ __attribute__((aligned(1024))) char kbuf0[KT];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[KT];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[VT];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[VT];
+  __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int bcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+            c32 = lane & 31;
+  const int N = a.N, Np = a.Np;
+  int bh, qt;
+  sched_decode(sc, gridDim.x, bh, qt);
+  const int q0 = qt * BR;
+  const uint8_t* __restrict__ K8 = a.k8 + (size_t)bh * N * D;
+  const uint8_t* __restrict__ VT8 = a.vt8 + (size_t)bh * D * Np;
+
+  // ---- key tiles this query block visits
+  const int nk = (N + BC - 1) / BC;
+  int ntiles = nk;
+  if (CAUSAL) ntiles = min(ntiles, (min(q0 + BR, N) - 1) / BC + 1);
+  if (SPARSE) {
+    const int qb = q0 / kMaskBlock;
+    const int hi = CAUSAL ? min(qb + 1, a.nb) : a.nb;
+    if (w == 0) {
+      const int cnt = build_block_list(a.mask, a.nb, qb, false, 0, hi, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = bcount;
+    ntiles = 2 * cnt;
+    if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BC >= N) ntiles -= 1;  // tail block half past N
+  }
+  auto tile_start = [&](int t) -> int {
+    if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
+    return t * BC;
+  };
+
+  // ---- Q operand (B): lane holds query q0 + 32 w + c32, features 64 f + 16 h .. and 64 f + 32 + 16 h ..
+  const int qrow = q0 + 32 * w + c32;
+  i32x8 qop[DF];
+  int qsc = 0;
+  {
+    const uint8_t* qr = a.q8 + ((size_t)bh * N + qrow) * D;
+#pragma unroll
+    for (int f = 0; f < DF; ++f) {
+      uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi4 = lo;
+      if (qrow < N) {
+        lo = *reinterpret_cast<const uint4*>(qr + 64 * f + 16 * h);
+        hi4 = *reinterpret_cast<const uint4*>(qr + 64 * f + 32 + 16 * h);
+      }
+      qop[f] = join16x2(lo, hi4);
+    }
+    if (qrow < N) {
+      const uint8_t* s = a.qs + ((size_t)bh * N + qrow) * NSB;
+      const uint32_t row = NSB == 4 ? *reinterpret_cast<const uint32_t*>(s) : *reinterpret_cast<const unsigned short*>(s);
+      qsc = (int)(row >> (8 * h));  // byte 2f: block 2f + h
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = zero16();
+  float m_used = neg_inf();  // running max in scaled log2 units
+  float lsum = 0.f;
+  const float sl = a.scale_log2;
+
+  // ---- per-lane LDS read offsets
+  int koff[2][DF][2];  // [kb][f][half]: K row 32 kb + pi(c32), chunks 4f + h and 4f + 2 + h
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int f = 0; f < DF; ++f)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 32 * kb + pi32(c32), ch = 4 * f + 2 * u + h;
+        koff[kb][f][u] = row * D + ((ch ^ sw_k8<D>(row)) << 4);
+      }
+  int voff[DB][2];  // V^T row 32 db + c32, chunks h and 2 + h
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 32 * db + c32, ch = 2 * u + h;
+      voff[db][u] = row * BC + ((ch ^ sw_v8(row)) << 4);
+    }
+  // ---- copy offsets: slot s = 64 (KI w + i) + lane of a tile
+  int kcopy[KI], vcopy[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int s = 64 * (KI * w + i) + lane, row = s / KCH, pch = s % KCH;
+    kcopy[i] = row * D + ((pch ^ sw_k8<D>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int s = 64 * (VI * w + i) + lane, row = s / 4, pch = s % 4;
+    vcopy[i] = row * Np + ((pch ^ sw_v8(row)) << 4);
+  }
+  auto issue_k = [&](char* buf, int k0) {
+    const Rsrc r = make_rsrc(K8 + (size_t)k0 * D, max(N - k0, 0) * D);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) dma16(r, buf + 1024 * (KI * w + i), kcopy[i], 0);
+  };
+  auto issue_v = [&](char* buf, int k0) {
+    const Rsrc r = make_rsrc(VT8 + k0, D * Np - k0);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) dma16(r, buf + 1024 * (VI * w + i), vcopy[i], 0);
+  };
+  // scale loads (registers): K rows of the two 32-key blocks, shifted so byte 2f is block 2f + h;
+  // V^T: the DB bytes of feature 32 db + c32 (db = byte) in key block k0/32 + h
+  const Rsrc ks_r = make_rsrc(a.ks + (size_t)bh * N * NSB, N * NSB);
+  const Rsrc vs_r = make_rsrc(a.vts + (size_t)bh * (Np / 32) * 32 * DB, (Np / 32) * 32 * DB);
+  auto load_ksc = [&](int k0, int (&out)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int off = (k0 + 32 * kb + pi32(c32)) * NSB;
+      const uint32_t row = NSB == 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ks_r, off, 0, 0)
+                                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks_r, off, 0, 0);
+      out[kb] = (int)(row >> (8 * h));
+    }
+  };
+  auto load_vsc = [&](int k0) -> int {
+    const int off = ((k0 / 32 + h) * 32 + c32) * DB;
+    return DB == 4 ? (int)__builtin_amdgcn_raw_buffer_load_b32(vs_r, off, 0, 0)
+                   : (int)(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vs_r, off, 0, 0);
+  };
+
+  // S^T for the two 32-key blocks of a tile: register r of lane half h = key k0 + 32 kb + 16 h + r
+  auto scores = [&](const char* tk, const int (&ksc)[2], f32x16(&s)[2]) {
+    s[0] = zero16();
+    s[1] = zero16();
+#pragma unroll
+    for (int f = 0; f < DF; ++f)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const i32x8 kop = join16x2(lds16(tk + koff[kb][f][0]), lds16(tk + koff[kb][f][1]));
+        s[kb] = mfma_mx_sel(2 * f, 2 * f, kop, qop[f], s[kb], ksc[kb], qsc);
+      }
+  };
+  auto mask_tile = [&](f32x16(&s)[2], int k0) {
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 16 * h + r;
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
+        }
+    }
+  };
+  auto update_max = [&](const f32x16(&s)[2], float& m, float& alpha) {
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmax_nan(mt, s[kb][r]);
+    mt = half_swap_max(mt) * sl;
+    const float m_new = (mt > m + kRescaleThresholdFp8) ? mt : m;
+    alpha = (m_new == m) ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
+  };
+
+  // Software pipeline (as the bf16 kernel): K copies and K scales two tiles ahead, V copies and
+  // V scales one tile ahead; the scores one tile ahead of the exponentials.
+  f32x16 sbuf[2][2];
+  // scale registers: at step t, ksc[t % 2] holds tile t+1 and ksc[(t + 1) % 2] receives tile
+  // t+2 (ksc[2] holds tile 0); vsc[t % 2] holds tile t and vsc[(t + 1) % 2] receives tile t+1
+  int ksc[3][2] = {{kP8Scale, kP8Scale}, {kP8Scale, kP8Scale}, {kP8Scale, kP8Scale}};
+  int vsc[2] = {kP8Scale, kP8Scale};
+  float alpha = 1.f;
+  if (ntiles > 0) {
+    issue_k(kbuf0, tile_start(0));
+    issue_v(vbuf0, tile_start(0));
+    load_ksc(tile_start(0), ksc[2]);
+    vsc[0] = load_vsc(tile_start(0));
+    if (ntiles > 1) {
+      issue_k(kbuf1, tile_start(1));
+      load_ksc(tile_start(1), ksc[0]);
+    }
+  }
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 0) {
+    scores(kbuf0, ksc[2], sbuf[0]);
+    mask_tile(sbuf[0], tile_start(0));
+    update_max(sbuf[0], m_used, alpha);
+    alpha = 1.f;  // nothing accumulated yet
+  }
+
+  auto step = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;  // t % 2
+    char* const k_next = par ? kbuf0 : kbuf1;      // holds K[t+1] (stale K on the last tile)
+    char* const k_free = par ? kbuf1 : kbuf0;      // held K[t]; receives K[t+2]
+    char* const v_cur = par ? vbuf1 : vbuf0;       // holds V[t]
+    char* const v_free = par ? vbuf0 : vbuf1;      // held V[t-1]; receives V[t+1]
+    f32x16(&s_cur)[2] = sbuf[par];
+    f32x16(&s_nxt)[2] = sbuf[par ^ 1];
+    int(&ksc_next)[2] = ksc[par];      // K scales of tile t+1
+    int(&ksc_free)[2] = ksc[par ^ 1];  // receives tile t+2
+    const int vsc_cur = vsc[par];
+    const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles;
+    if (has2) {
+      issue_k(k_free, tile_start(t + 2));
+      load_ksc(tile_start(t + 2), ksc_free);
+    }
+    if (has1) {
+      issue_v(v_free, tile_start(t + 1));
+      vsc[par ^ 1] = load_vsc(tile_start(t + 1));
+    }
+
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      lsum *= alpha;
+    }
+    const float msub = (m_used == neg_inf()) ? 0.f : m_used;
+
+    // section 1: S[t+1] on the matrix cores; P[t] = exp2(S[t] * scale * log2(e) - m) in fp32
+    // (kept in s_cur for the row sums) and as E4M3 codes for PV: byte 16 kb + r of the operand
+    // is register r of block kb.  Each MFMA is followed by a share of the exponentials.
+    constexpr int NS = 2 * DF;
+    constexpr int EPS = 32 / NS;
+    i32x8 pop;
+    {
+      s_nxt[0] = zero16();
+      s_nxt[1] = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int f = i >> 1, kb = i & 1;
+        const i32x8 kop = join16x2(lds16(k_next + koff[kb][f][0]), lds16(k_next + koff[kb][f][1]));
+        s_nxt[kb] = mfma_mx_sel(2 * f, 2 * f, kop, qop[f], s_nxt[kb], ksc_next[kb], qsc);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int j = i * EPS + e;
+          s_cur[j >> 4][j & 15] = fast_exp2(__builtin_fmaf(s_cur[j >> 4][j & 15], sl, -msub));
+        }
+#pragma unroll
+        for (int e = 0; e < EPS; e += 4) {
+          const int j = i * EPS + e;
+          int r = __builtin_amdgcn_cvt_pk_fp8_f32(s_cur[j >> 4][j & 15], s_cur[j >> 4][(j & 15) + 1], 0, false);
+          r = __builtin_amdgcn_cvt_pk_fp8_f32(s_cur[j >> 4][(j & 15) + 2], s_cur[j >> 4][(j & 15) + 3], r, true);
+          pop[j >> 2] = r;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // pin P[t] here: without a use in this section the compiler sinks the exponentials past the
+    // mask branch below, away from the MFMAs they are meant to run beside
+    asm volatile("" : "+v"(pop));
+    asm volatile("" : "+v"(s_cur[0]), "+v"(s_cur[1]));
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (has1) mask_tile(s_nxt, tile_start(t + 1));
+
+    // section 2: O^T += V^T P^T over the 64 keys, the row sums of P[t], the max after S[t+1]
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i32x8 vop = join16x2(lds16(v_cur + voff[db][0]), lds16(v_cur + voff[db][1]));
+      oacc[db] = mfma_mx_sel(db, 0, vop, pop, oacc[db], vsc_cur, kP8Scale);
+    }
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[r & 3] += s_cur[kb][r];
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+    asm volatile("" : "+v"(lsum));
+    {
+      float m_nx = m_used, a_nx;
+      update_max(s_nxt, m_nx, a_nx);
+      asm volatile("" : "+v"(m_nx), "+v"(a_nx));
+      m_used = has1 ? m_nx : m_used;
+      alpha = has1 ? a_nx : alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_dma();
+    __syncthreads();
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, IC<0>{});
+    if (t + 1 < ntiles) step(t + 1, IC<1>{});
+  }
+
+  // ---- epilogue: lane holds features 32 db + 8 g + 4 h + e of query qrow in register 4 g + e
+  const float ltot = half_swap_sum(lsum);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (qrow < N) {
+    __bf16* orow = a.o + ((size_t)bh * N + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = v4;
+      }
+    if (h == 0) a.lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m_used + __log2f(ltot)) * kLn2 : neg_inf();
+  }
+}
+
+}  // namespace
+
+template <int D, bool C, bool S>
+static hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t st) {
+  constexpr int BR = 128;
+  const int nq = (a.N + BR - 1) / BR;
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_mxfp8_kernel<D, C, S>));
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  hipLaunchKernelGGL((fwd_mxfp8_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mxfp8(const Fp8FwdArgs& a, hipStream_t stream) {
+  const bool causal = a.causal != 0, sparse = a.mask != nullptr;
+  if (a.d == 64) {
+    if (causal) return sparse ? launch_fp8_t<64, true, true>(a, stream) : launch_fp8_t<64, true, false>(a, stream);
+    return sparse ? launch_fp8_t<64, false, true>(a, stream) : launch_fp8_t<64, false, false>(a, stream);
+  }
+  if (causal) return sparse ? launch_fp8_t<128, true, true>(a, stream) : launch_fp8_t<128, true, false>(a, stream);
+  return sparse ? launch_fp8_t<128, false, true>(a, stream) : launch_fp8_t<128, false, false>(a, stream);
+}
+
+hipError_t launch_mxfp8_quantize_rows(const __bf16* x, uint8_t* codes, uint8_t* scales, long long rows, int d,
+                                      hipStream_t st) {
+  const long long nblocks = rows * (d / 32);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st, x, codes,
+                     scales, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_quantize_vt(const __bf16* v, uint8_t* codes_t, uint8_t* scales_t, int BH, int N, int d,
+                                    hipStream_t st) {
+  const int Np = fp8_vt_cols(N);
+  const dim3 grid(Np / 64, BH);
+  if (d == 64)
+    hipLaunchKernelGGL((mx_quantize_vt_kernel<64>), grid, dim3(256), 0, st, v, codes_t, scales_t, N, Np);
+  else
+    hipLaunchKernelGGL((mx_quantize_vt_kernel<128>), grid, dim3(256), 0, st, v, codes_t, scales_t, N, Np);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -105,6 +105,53 @@ int flash_attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                            const uint8_t *block_mask, int splits,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* MX-FP8 forward (the FP8 variant of the forward named in "How FlashAttention Bypasses the GPU
+ * Memory Bottleneck to Enable Long-Context AI", on FlashAttention-3).  Same definition as
+ * flash_attn_fwd, computed from MX-FP8 inputs (OCP Microscaling Formats v1.0: E4M3 element codes,
+ * one E8M0 scale byte 2^(s - 127) per block of 32 consecutive elements along the contraction
+ * index) on the scaled FP8 matrix cores, fp32 accumulation and softmax.  The exact result is
+ * attention over the dequantised inputs; the kernel adds the rounding of P (values <= 2^8) to
+ * E4M3 before the P V product, so each O element is within
+ *   sum_j max(2^-4 p_j, 2^-10) |v_j| / sum_j p_j   (p the softmax weights, max_j p_j = 1)
+ * of it, plus fp32 rounding; LSE uses P in fp32 and keeps fp32 accuracy.
+ *   q8, k8     in  E4M3 codes [B, H, N, d]              (flash_attn_mxfp8_quantize_rows)
+ *   q_scales, k_scales  in  E8M0 [B, H, N, d / 32], block c of a row = elements 32c .. 32c + 31
+ *   vt8        in  E4M3 codes of V transposed, [B, H, d, Np], Np = flash_attn_mxfp8_vt_cols(N),
+ *                  columns >= N zero                    (flash_attn_mxfp8_quantize_vt)
+ *   vt_scales  in  E8M0, blocks of 32 keys: scale of feature f, keys 32j .. 32j + 31 of head
+ *                  (b, h) at byte (((b H + h) Np/32 + j) 32 + f % 32) (d/32) + f / 32
+ *   o          out bf16 [B, H, N, d];  lse  out float32 [B, H, N]
+ *   B, H, N, d, scale, causal, block_mask   as flash_attn_fwd
+ * All pointers 16-byte aligned device memory; outputs must not overlap inputs (FA_ERR_ALIAS).
+ */
+int flash_attn_fwd_mxfp8(const uint8_t *q8, const uint8_t *q_scales, const uint8_t *k8,
+                         const uint8_t *k_scales, const uint8_t *vt8, const uint8_t *vt_scales,
+                         void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
+                         const uint8_t *block_mask, hipStream_t stream);
+
+/* MX-FP8 quantisation (OCP MX v1.0, section 6.3) of a bf16 [B, H, N, d] tensor in blocks of 32
+ * along d, for Q and K: per block, shared exponent e = floor(log2(max |x|)) - 8 held to
+ * [-127, 127] (a zero block takes -127), scale byte e + 127, codes = x * 2^-e rounded to
+ * nearest-even E4M3 after clamping to +-448.  Inputs must be finite.
+ *   x       in   bf16 [B, H, N, d];  d in {64, 128}
+ *   codes   out  E4M3 [B, H, N, d];  scales  out  E8M0 [B, H, N, d / 32]
+ */
+int flash_attn_mxfp8_quantize_rows(const void *x, uint8_t *codes, uint8_t *scales,
+                                   int B, int H, int N, int d, hipStream_t stream);
+
+/* Columns of the transposed V layout: N rounded up to a multiple of 64 (0 if N < 1). */
+int64_t flash_attn_mxfp8_vt_cols(int N);
+
+/* MX-FP8 quantisation of V into the transposed layout flash_attn_fwd_mxfp8 reads: blocks of 32
+ * consecutive keys per feature, same rule as flash_attn_mxfp8_quantize_rows; keys N .. Np - 1
+ * are zero (code 0) and take part in their block as zeros.
+ *   v          in   bf16 [B, H, N, d]
+ *   codes_t    out  E4M3 [B, H, d, Np];  scales_t  out  E8M0, B * H * Np * d / 32 bytes, laid
+ *                   out as described at flash_attn_fwd_mxfp8
+ */
+int flash_attn_mxfp8_quantize_vt(const void *v, uint8_t *codes_t, uint8_t *scales_t,
+                                 int B, int H, int N, int d, hipStream_t stream);
+
 /* Log-sum-exp merge of `parts` partial results computed over disjoint key sets of the same
  * query rows (the partials of a split-key forward, or of key shards held by different
  * devices).  Per row: LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, the softmax

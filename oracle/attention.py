@@ -87,6 +87,36 @@ def forward_head(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
     return O, lse
 
 
+def p_rounding_bound(q, k, v, scale, causal=False, block_mask=None, rows=None, rel=2.0 ** -4, floor=2.0 ** -10,
+                     chunk=1024):
+    """Elementwise bound [len(rows), d] on |sum_j p'_j v_j / sum_j p_j - O| when every visible
+    weight p_j = exp(S_ij - max_j S_ij) (so max_j p_j = 1) is replaced in the numerator only by
+    some p'_j with |p'_j - p_j| <= max(rel p_j, floor):  sum_j max(rel p_j, floor) |v_j| / sum_j p_j
+    over the visible keys (triangle inequality, attained by the worst-signed perturbation).
+
+    With rel = 2^-4 and floor = 2^-10 it bounds the rounding of P to E4M3 before the P V product
+    in the MX-FP8 forward: E4M3 keeps 3 fraction bits (half an ulp is at most 2^-4 of a normal
+    value) and its subnormal step is 2^-9 (rounding error at most 2^-10), for weights held as
+    c p_j with c >= 1 (the kernel's running-max offset never exceeds the row max), which only
+    shrinks the floor in units of p.  Dead rows get 0."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    out = np.zeros((rows.size, v.shape[1]))
+    absv = np.abs(v)
+    for a in range(0, rows.size, chunk):
+        r = rows[a:a + chunk]
+        S = _scores(q, k, r, scale, causal, block_mask)
+        vis = np.isfinite(S)
+        m = np.where(vis.any(axis=1), S.max(axis=1), 0.0)
+        p = np.where(vis, np.exp(S - m[:, None]), 0.0)
+        err = np.where(vis, np.maximum(rel * p, floor), 0.0)
+        den = p.sum(axis=1)
+        out[a:a + r.size] = (err @ absv) / np.where(den > 0, den, 1.0)[:, None]
+    return out
+
+
 def forward(q, k, v, scale, causal=False, block_mask=None, chunk=1024):
     """[B, H, N, d] inputs -> O [B, H, N, d], LSE [B, H, N] (fp64)."""
     B, H, N, d = q.shape

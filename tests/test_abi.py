@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     for n in ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_f32", "flash_attn_bwd_f32",
               "flash_attn_bwd_workspace_bytes", "flash_attn_status_string", "flash_attn_bwd_preprocess",
               "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_fwd_splitkv",
-              "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_merge"):
+              "flash_attn_fwd_splitkv_workspace_bytes", "flash_attn_merge", "flash_attn_fwd_mxfp8",
+              "flash_attn_mxfp8_quantize_rows", "flash_attn_mxfp8_quantize_vt", "flash_attn_mxfp8_vt_cols"):
         assert n in names, n
 
 
@@ -230,3 +231,41 @@ def test_merge_argument_errors(L):
     assert call(o=ctypes.c_void_p(o.value + 8)) == fa.FA_ERR_ALIGN
     assert call(o=ctypes.c_void_p(op.value + 1024)) == fa.FA_ERR_ALIAS
     assert call(lse=ctypes.c_void_p(o.value + 64)) == fa.FA_ERR_ALIAS
+
+
+def test_mxfp8_vt_cols(L):
+    import exact_io_aware_flash_amd as fa
+    assert [fa.mxfp8_vt_cols(n) for n in (0, 1, 63, 64, 65, 128, 16384, 16385)] == [0, 64, 64, 64, 128, 128, 16384,
+                                                                                   16448]
+
+
+def test_mxfp8_argument_errors(L):
+    import exact_io_aware_flash_amd as fa
+    q8, qs, k8, ks, vt, vs, o, lse = ptrs(8)
+
+    def fwd8(*args, B=1, H=1, N=128, d=64, scale=0.125, causal=0, mask=None):
+        a = list(args) if args else [q8, qs, k8, ks, vt, vs, o, lse]
+        return L.flash_attn_fwd_mxfp8(*a, B, H, N, d, scale, causal, mask, None)
+
+    base = [q8, qs, k8, ks, vt, vs, o, lse]
+    for i in range(8):
+        a = list(base)
+        a[i] = None
+        assert fwd8(*a) == fa.FA_ERR_NULL, i
+    assert fwd8(N=0) == fa.FA_ERR_SHAPE
+    assert fwd8(d=96) == fa.FA_ERR_HEADDIM
+    assert fwd8(scale=0.0) == fa.FA_ERR_SCALE
+    assert fwd8(causal=2) == fa.FA_ERR_FLAG
+    a = list(base)
+    a[2] = ctypes.c_void_p((1 << 40) + 2 * BIG + 8)
+    assert fwd8(*a) == fa.FA_ERR_ALIGN
+    a = list(base)
+    a[6] = a[4]  # output over V's codes
+    assert fwd8(*a) == fa.FA_ERR_ALIAS
+    x, c, sc = ptrs(3)
+    for fn in (L.flash_attn_mxfp8_quantize_rows, L.flash_attn_mxfp8_quantize_vt):
+        assert fn(None, c, sc, 1, 1, 128, 64, None) == fa.FA_ERR_NULL
+        assert fn(x, c, sc, 1, 1, 128, 48, None) == fa.FA_ERR_HEADDIM
+        assert fn(x, c, sc, 1, 0, 128, 64, None) == fa.FA_ERR_SHAPE
+        assert fn(x, x, sc, 1, 1, 128, 64, None) == fa.FA_ERR_ALIAS
+        assert fn(x, ctypes.c_void_p((1 << 40) + BIG + 4), sc, 1, 1, 128, 64, None) == fa.FA_ERR_ALIGN

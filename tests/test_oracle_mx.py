@@ -80,3 +80,52 @@ def test_dequantised_error_bound_and_zero_blocks():
     assert np.all(np.abs(deq[~inside]) == 448 * X[~inside])
     z, zs = mx.quantize(np.zeros((2, 64)))
     assert np.all(z == 0) and np.all(zs == 0)
+
+
+def _head(seed, N=48, d=8):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((N, d)), rng.standard_normal((N, d)), rng.standard_normal((N, d))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p_rounding_bound_is_attained_by_worst_perturbation(causal):
+    # the bound is the triangle inequality: the perturbation p'_j = p_j + sign(v_jf) max(2^-4 p_j,
+    # 2^-10) reaches it exactly for feature f, and random admissible perturbations stay inside
+    import oracle
+    q, k, v = _head(11)
+    scale = 0.7
+    rows = np.arange(q.shape[0])
+    bound = oracle.p_rounding_bound(q, k, v, scale, causal)
+    O, _ = oracle.forward_head(q, k, v, scale, causal)
+    S = scale * (q @ k.T)
+    vis = oracle.visible(rows, rows, causal, None)
+    S = np.where(vis, S, -np.inf)
+    p = np.where(vis, np.exp(S - S.max(axis=1, keepdims=True)), 0.0)
+    err = np.where(vis, np.maximum(2.0 ** -4 * p, 2.0 ** -10), 0.0)
+    for f in range(v.shape[1]):
+        pw = p + err * np.sign(v[:, f])[None, :]
+        got = (pw @ v[:, f]) / p.sum(axis=1)
+        assert np.allclose(np.abs(got - O[:, f]), bound[:, f], rtol=1e-12, atol=1e-15)
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        pw = p + err * rng.uniform(-1, 1, p.shape)
+        dev = np.abs((pw @ v) / p.sum(axis=1, keepdims=True) - O)
+        assert np.all(dev <= bound * (1 + 1e-12) + 1e-15)
+
+
+@pytest.mark.parametrize("c", [1.0, 3.7, 2.0 ** 8])
+def test_p_rounding_bound_covers_e4m3_rounding_of_p(c):
+    # P held as c p (1 <= c <= 2^8, so every value stays <= 448) and rounded to E4M3 in the
+    # numerator: the error stays within the bound, and uses a fair part of it (not vacuous)
+    import oracle
+    q, k, v = _head(12, N=200, d=16)
+    scale = 1.3
+    bound = oracle.p_rounding_bound(q, k, v, scale, True)
+    O, _ = oracle.forward_head(q, k, v, scale, True)
+    P = oracle.probabilities(q, k, scale, True)
+    p = P / P.max(axis=1, keepdims=True)
+    pq = mx.e4m3_decode(mx.e4m3_encode(c * p)) / c
+    got = (pq @ v) / p.sum(axis=1, keepdims=True)
+    dev = np.abs(got - O)
+    assert np.all(dev <= bound * (1 + 1e-12))
+    assert dev.max() > 0.05 * bound.max()
