@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 flop/clk x 2.4 GHz (dense)
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 8192 fp8 flop/clk x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s (bf16, d=64/128) and % of MI355X MFMA peak"
 CSRC = os.path.join(ROOT, "exact_io_aware_flash_amd", "csrc")
@@ -269,6 +270,55 @@ def cpu_baseline(w, t, heads: int):
     }
 
 
+def fp8_forward(fa, w, q, k, v, mask, flops, iters):
+    """The MX-FP8 forward on the same inputs, as a separate figure (not the metric): the
+    quantisation of Q, K (row blocks) and V (transposed) and the forward, each timed with events
+    on the library's stream."""
+    import torch
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(n):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    Q8, K8, V8 = fa.mxfp8_quantize(q), fa.mxfp8_quantize(k), fa.mxfp8_quantize(v, transposed=True)
+    o8, l8 = fa.fwd_mxfp8(Q8, K8, V8, w.scale, w.causal, mask)
+    ms = timed(lambda: fa.fwd_mxfp8(Q8, K8, V8, w.scale, w.causal, mask, out=o8, lse=l8), iters)
+    qms = timed(lambda: (fa.mxfp8_quantize(q), fa.mxfp8_quantize(k), fa.mxfp8_quantize(v, transposed=True)), iters)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "TFLOP/s": tf, "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "quantize_qkv_ms": qms, "TFLOP/s_with_quantize": flops / ((ms + qms) * 1e-3) / 1e12,
+            "dtype": "MX-FP8 E4M3 operands, fp32 accumulation and softmax"}
+
+
+def fp8_cpu_baseline(w, t):
+    """The oracle of the FP8 forward on the host: host MX-FP8 quantisation of one head, then the
+    fp64 forward on the dequantised inputs."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    from oracle import mx
+
+    f = lambda name: workloads.bf16_bits_to_f32(getattr(t, name)[0, 0]).astype(np.float64)
+    t0 = time.perf_counter()
+    qd = mx.dequantize(*mx.quantize(f("q"), axis=-1), axis=-1)
+    kd = mx.dequantize(*mx.quantize(f("k"), axis=-1), axis=-1)
+    vd = mx.dequantize(*mx.quantize(f("v"), axis=0), axis=0)
+    oracle.forward_head(qd, kd, vd, w.scale, w.causal, t.block_mask)
+    dt = time.perf_counter() - t0
+    return {"value": workloads.flops_fwd(1, 1, w.N, w.d, w.causal, t.block_mask) / dt / 1e12, "unit": "TFLOP/s",
+            "kind": "oracle", "sample": f"head (0,0): host MX-FP8 quantisation + fp64 forward, {dt:.1f} s",
+            "seconds": dt}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +326,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the MX-FP8 forward figure")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="copy MIB MiB with the runtime's copy kernel before the bench (counter scaling)")
@@ -416,6 +467,10 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    if not args.no_fp8:
+        line["mxfp8_forward"] = fp8_forward(fa, w, q, k, v, mask, ff, max(3, args.steps))
+        if not args.no_cpu_baseline:
+            line["mxfp8_forward"]["cpu_baseline"] = fp8_cpu_baseline(w, t)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_heads)
     print(json.dumps(line), flush=True)
