@@ -70,7 +70,8 @@ def preprocess_bytes(w):
 
 
 KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_delta_kernel": "bwd_preprocess",
-               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq"}
+               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "fwd_mxfp8_kernel": "fwd_mxfp8",
+               "mx_quantize_rows_kernel": "mxfp8_quantize_rows", "mx_quantize_vt_kernel": "mxfp8_quantize_vt"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -293,7 +294,9 @@ def fp8_forward(fa, w, q, k, v, mask, flops, iters):
     ms = timed(lambda: fa.fwd_mxfp8(Q8, K8, V8, w.scale, w.causal, mask, out=o8, lse=l8), iters)
     qms = timed(lambda: (fa.mxfp8_quantize(q), fa.mxfp8_quantize(k), fa.mxfp8_quantize(v, transposed=True)), iters)
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms": ms, "TFLOP/s": tf, "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS,
+    return {"ms": ms, "TFLOP/s": tf, "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "roofline": {"kernel": "fwd_mxfp8", "bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS, "traffic": traffic_for("fwd_mxfp8", w.name)},
             "quantize_qkv_ms": qms, "TFLOP/s_with_quantize": flops / ((ms + qms) * 1e-3) / 1e12,
             "dtype": "MX-FP8 E4M3 operands, fp32 accumulation and softmax"}
 

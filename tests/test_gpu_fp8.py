@@ -198,7 +198,14 @@ def test_fwd_mxfp8_dead_rows(dev):
 
 
 def test_fwd_mxfp8_long_sampled(dev):
-    # the long-context shape (N = 16384, d = 128, causal) on 4 heads, sampled rows of 2 heads
-    t = workloads.random_case(1, 4, 16384, 128, "bf16", seed=1004, with_do=False)
+    # the long-context shape (N = 16384, d = 128, causal) on 8 heads: B*H a multiple of 8 takes the
+    # XCD remap and, with 128 query tiles per head, the head-major order; sampled rows of 2 heads
+    t = workloads.random_case(1, 8, 16384, 128, "bf16", seed=1004, with_do=False)
     rows = G.sample_rows(16384, 48, seed=9)
-    _fp8_case("long sampled", t, 1.0 / np.sqrt(128), True, dev, [(0, 0), (0, 3)], rows=rows)
+    _fp8_case("long sampled", t, 1.0 / np.sqrt(128), True, dev, [(0, 0), (0, 7)], rows=rows)
+
+
+def test_fwd_mxfp8_remapped_grid(dev):
+    # B*H = 16 (remapped grid, level order), d = 64, non-causal, every row compared on 2 heads
+    t = workloads.random_case(2, 8, 1024, 64, "bf16", seed=3201, with_do=False)
+    _fp8_case("remapped grid", t, 0.125, False, dev, [(0, 3), (1, 6)])
