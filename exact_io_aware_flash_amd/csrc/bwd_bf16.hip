@@ -174,21 +174,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   // sinking the LDS reads next to their uses, where their latency would stall the MFMA pipe).
   auto half = [&](auto maskc, const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
     constexpr bool MASK = decltype(maskc)::value;
-    // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`
-    f32x16 sacc = zero16(), pacc = zero16();
+    // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`.
+    // Accumulated in VGPRs by inline-asm MFMAs: this kernel's compiled MFMAs accumulate in AGPRs
+    // (its dK / dV accumulators need them), where every VALU read of S or dP below would cost a
+    // v_accvgpr_read.  The asm is opaque to the compiler's hazard tracking, so the wait states an
+    // MFMA result needs before a VALU instruction reads it (14 on gfx950) are issued explicitly.
+    // Operand reads run two MFMA pairs ahead of their use (fenced, so they stay there).
+    f32x16 sacc, pacc;
+    {
+      bf16x8 qa[DC], oa[DC];
+      auto rd = [&](int c) {
+        qa[c] = lds_b128(tq + raddr[c] + 32 * s * D * 2);
+        oa[c] = lds_b128(to + raddr[c] + 32 * s * D * 2);
+      };
+      rd(0);
+      rd(1);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      sacc = mfma32(lds_b128(tq + raddr[c] + 32 * s * D * 2), kreg[c], sacc);
-      pacc = mfma32(lds_b128(to + raddr[c] + 32 * s * D * 2), vreg[c], pacc);
+      for (int c = 0; c < DC; ++c) {
+        if (c + 2 < DC) rd(c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(oa[0]), "v"(vreg[0]));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(oa[c]), "v"(vreg[c]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
     }
-    // operand reads run two MFMA pairs ahead of the MFMAs that consume them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int c = 0; c < DC - 2; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
     bf16x8 pp[2], dsp[2];
 #pragma unroll

@@ -44,23 +44,11 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 // ---------------------------------------------------------------------------------------------
-// LDS tiles.  Every MFMA operand is fetched with 16-byte ds_read_b128 (LDS serves these 16 lanes
-// per pass over a 256-byte bank window; the 8-byte transposing read ds_read_b64_tr_b16 moves
-// data at about a quarter of that rate on gfx950, so operands that need the contraction index
-// inside a lane are written transposed into their own tile when the tile is staged instead).
-//
-// A Tile<ROWS, COLS> holds ROWS rows of COLS bf16 with a row stride of COLS*2 + 16 bytes.  The
-// extra 16 bytes shift consecutive rows by one 16-byte bank slot (mod 256 bytes), so 16 lanes
-// reading the same column of 16 different rows of a 32-row group hit 16 distinct slots; and every
-// address is a per-lane base plus a compile-time offset.
+// LDS operand reads.  Row operands use 16-byte ds_read_b128 (LDS serves 16 lanes per pass over a
+// 256-byte bank window); operands that need the contraction index inside a lane use the 8-byte
+// transposing ds_read_b64_tr_b16, which a conflict-free probe on gfx950 measured at about 0.7 of
+// the row-read bandwidth.
 // ---------------------------------------------------------------------------------------------
-template <int ROWS, int COLS>
-struct Tile {
-  static constexpr int STRIDE = COLS * 2 + 16;
-  static constexpr int BYTES = ROWS * STRIDE;
-  __device__ static constexpr int off(int r, int c) { return r * STRIDE + c * 2; }
-};
-
 __device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Transposing 8-byte LDS read: within each 16-lane group, lane i receives element i % 4 of the
@@ -93,12 +81,6 @@ constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit data, no format conversion
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
-}
-__device__ __forceinline__ uint4 load16(const Rsrc& r, int byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-__device__ __forceinline__ uint2 load8(const Rsrc& r, int byte_off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -169,105 +151,15 @@ struct DmaTile {
   }
 };
 
-// A slab of a feature-major copy: R feature rows x C consecutive positions (columns), the
-// global rows `stride` elements apart.  Same chunk swizzle as DmaTile<., C>; each row is read
-// 16 bytes per lane (16 lanes = 16 consecutive rows at one chunk: distinct bank slots).
-template <int R, int C>
-struct SlabDma {
-  static constexpr int CPR = C / 8;
-  static constexpr int BYTES = R * C * 2;
-  static constexpr int CH = R * CPR / 256;
-  static_assert(CH >= 1 && (R * CPR) % 256 == 0, "slab too small for 4 waves");
-  __device__ static constexpr int off(int row, int col) { return row * C * 2 + (((col >> 3) ^ sw_dual<C>(row)) << 4); }
-  int voff[CH];
-  __device__ __forceinline__ void init(int w, int lane, int stride) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = 64 * (CH * w + i) + lane;
-      const int row = slot / CPR, pchunk = slot % CPR;
-      voff[i] = (row * stride + ((pchunk ^ sw_dual<C>(row)) << 3)) * 2;
-    }
-  }
-  // enqueue columns [col0, col0 + C) of every row of the copy at `head` (R rows of `stride`
-  // elements; col0 + C <= stride) into `tile`
-  __device__ __forceinline__ void issue(const __bf16* head, int stride, char* tile, int col0, int w) const {
-    const Rsrc r = make_rsrc(head + col0, (R * stride - col0) * 2);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) dma16(r, tile + 1024 * (CH * w + i), voff[i], 0);
-  }
-};
-
-// Row-major staging of R rows x D columns (rows >= N read as zero): 16-byte global loads into
-// registers, then 16-byte LDS stores.  Split in two so the loads for the next tile can be in
-// flight while the current tile is being used.
-template <int R, int D>
-struct RowStage {
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int CH = R * D / 8 / 256;    // chunks per thread
-  static_assert(CH >= 1 && (R * D / 8) % 256 == 0, "tile too small for 256 threads");
-  uint4 reg[CH];
-  __device__ __forceinline__ void load(const Rsrc& src, int row0, int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      reg[i] = load16(src, ((row0 + row) * D + col) * 2);
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / CPR, col = (cidx % CPR) * 8;
-      *reinterpret_cast<uint4*>(tile + Tile<R, D>::off(row, col)) = reg[i];
-    }
-  }
-};
-
-// Transposed staging: R rows x D columns of global memory land as Tile<D, R> (column c of the
-// source becomes LDS row c).  Each of the first (R/8)*(D/4) threads moves one 8-row x 4-column
-// block: eight 8-byte loads, a 16-bit transpose in registers, four 16-byte LDS stores.
-template <int R, int D>
-struct TransStage {
-  static constexpr int RG = R / 8;            // row groups
-  static constexpr int NB = RG * (D / 4);     // blocks
-  static_assert(NB <= 256, "one block per thread");
-  uint2 reg[8];
-  __device__ __forceinline__ void load(const Rsrc& src, int row0, int tid) {
-    if (tid < NB) {
-      const int rg = tid % RG, cg = tid / RG;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) reg[e] = load8(src, ((row0 + 8 * rg + e) * D + 4 * cg) * 2);
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, int tid) const {
-    if (tid < NB) {
-      const int rg = tid % RG, cg = tid / RG;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 o;
-        unsigned* ow = reinterpret_cast<unsigned*>(&o);
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const unsigned x = (c < 2) ? reg[2 * wd].x : reg[2 * wd].y;
-          const unsigned y = (c < 2) ? reg[2 * wd + 1].x : reg[2 * wd + 1].y;
-          ow[wd] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        *reinterpret_cast<uint4*>(tile + Tile<D, R>::off(4 * cg + c, 8 * rg)) = o;
-      }
-    }
-  }
-};
+// maximum that propagates NaN (IEEE maximum): unlike fmaxf it needs no canonicalising moves of
+// its operands, and three of them fuse into one v_maximum3_f32
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // ---------------------------------------------------------------------------------------------
 // wave64 cross-half reductions: lanes l and l ^ 32 hold partial results for the same query.
 // v_permlane32_swap exchanges the upper half of its first operand with the lower half of its
 // second; called with (x, x) every lane ends up holding both its own value and its partner's.
 // ---------------------------------------------------------------------------------------------
-// maximum that propagates NaN (IEEE maximum): unlike fmaxf it needs no canonicalising moves of
-// its operands, and three of them fuse into one v_maximum3_f32
-__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
