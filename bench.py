@@ -75,6 +75,17 @@ KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_delta_kernel": "bwd_preprocess",
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def kernel_label(name: str):
+    """Short label of a library kernel from its profiler name (None for other kernels); the bf16
+    forward without the causal mask is labelled apart from the causal one."""
+    for key, short in KERNEL_KEYS.items():
+        if key in name:
+            if short == "fwd" and "<" in name and name.split("<", 1)[1].split(",")[1].strip() == "false":
+                return "fwd_noncausal"
+            return short
+    return None
+
+
 def read_counter(path: str, counter: str):
     """{dispatch id: (kernel name, counter value summed over the rows of that dispatch)}."""
     import csv
@@ -107,9 +118,9 @@ def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_mib: int = 
         factor = copy_bytes / (statistics.median(copies) * 1024.0)
         out[counter.lower() + "_factor"] = factor
         for name, v in vals.values():
-            for key, short in KERNEL_KEYS.items():
-                if key in name:
-                    per_kernel.setdefault(short, {}).setdefault(counter, []).append(v * 1024.0 * factor)
+            short = kernel_label(name)
+            if short:
+                per_kernel.setdefault(short, {}).setdefault(counter, []).append(v * 1024.0 * factor)
     lines = [f"| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | HBM bytes/launch |",
              "|---|---|---|---|---|"]
     for short, c in per_kernel.items():
@@ -196,11 +207,11 @@ def mfma_from(csv_path: str) -> str:
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     out = {}
     for e in per.values():
-        for key, short in KERNEL_KEYS.items():
-            if key in e["name"] and "SQ_VALU_MFMA_BUSY_CYCLES" in e:
-                cycles = e["GRBM_GUI_ACTIVE"] / 8.0  # per XCD
-                util = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * cycles) if cycles else 0.0
-                out.setdefault(short, []).append((util, cycles / (e["ns"] * 1e-9) / 1e9, e.get("SQ_INSTS_MFMA", 0.0)))
+        short = kernel_label(e["name"])
+        if short and "SQ_VALU_MFMA_BUSY_CYCLES" in e:
+            cycles = e["GRBM_GUI_ACTIVE"] / 8.0  # per XCD
+            util = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * cycles) if cycles else 0.0
+            out.setdefault(short, []).append((util, cycles / (e["ns"] * 1e-9) / 1e9, e.get("SQ_INSTS_MFMA", 0.0)))
     lines = ["| kernel | dispatches | MFMA busy ÷ (1024 SIMDs × kernel cycles) | kernel clock from GRBM_GUI_ACTIVE ÷ duration | "
              "MFMA instructions |", "|---|---|---|---|---|"]
     for short, v in out.items():
@@ -221,6 +232,10 @@ def traffic_for(kernel: str, workload: str):
         return None
     if rec.get("csrc_sha256") != csrc_digest():
         return None
+    import workloads
+
+    if kernel == "fwd" and not workloads.WORKLOADS[workload].causal:
+        kernel = "fwd_noncausal"
     for k in rec.get("kernels", []):
         if k.get("kernel") == kernel and k.get("workload") == workload:
             return k.get("hbm_bytes_per_launch")
@@ -470,6 +485,21 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    if w.causal and mask is None:
+        # the same shape without the causal mask (a figure beside the metric, not part of it)
+        fnc = workloads.flops_fwd(B, H, N, d, False, None)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(2):
+            fa.fwd(q, k, v, w.scale, False, None, out=o, lse=lse)
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(max(3, args.steps // 2)):
+            fa.fwd(q, k, v, w.scale, False, None, out=o, lse=lse)
+        e[1].record()
+        torch.cuda.synchronize()
+        ms_nc = e[0].elapsed_time(e[1]) / max(3, args.steps // 2)
+        tf_nc = fnc / (ms_nc * 1e-3) / 1e12
+        line["fwd_noncausal"] = {"ms": ms_nc, "TFLOP/s": tf_nc, "frac_of_peak": tf_nc / PEAK_BF16_TFLOPS}
     if not args.no_fp8:
         line["mxfp8_forward"] = fp8_forward(fa, w, q, k, v, mask, ff, max(3, args.steps))
         if not args.no_cpu_baseline:
