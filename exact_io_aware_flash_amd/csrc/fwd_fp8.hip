@@ -444,25 +444,40 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
 
     if (has1) mask_tile(s_nxt, tile_start(t + 1));
 
-    // section 2: O^T += V^T P^T over the 64 keys, the row sums of P[t], the max after S[t+1]
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i32x8 vop = join16x2(lds16(v_cur + voff[db][0]), lds16(v_cur + voff[db][1]));
-      oacc[db] = mfma_mx_sel(db, 0, vop, pop, oacc[db], vsc_cur, kP8Scale);
-    }
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part[r & 3] += s_cur[kb][r];
-    lsum += (part[0] + part[1]) + (part[2] + part[3]);
-    asm volatile("" : "+v"(lsum));
+    // section 2: O^T += V^T P^T over the 64 keys, the row sums of P[t], the max after S[t+1].
+    // Written out slot by slot like section 1: each PV MFMA is followed by its share of the row
+    // sums and of the running max (V operands read one MFMA ahead).
     {
-      float m_nx = m_used, a_nx;
-      update_max(s_nxt, m_nx, a_nx);
+      constexpr int EPD = 32 / DB;  // elements per slot
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      float mt = s_nxt[0][0];
+      auto vread = [&](int db) { return join16x2(lds16(v_cur + voff[db][0]), lds16(v_cur + voff[db][1])); };
+      i32x8 vop[DB];
+      vop[0] = vread(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + 1 < DB) vop[db + 1] = vread(db + 1);
+        oacc[db] = mfma_mx_sel(db, 0, vop[db], pop, oacc[db], vsc_cur, kP8Scale);
+#pragma unroll
+        for (int e = 0; e < EPD; ++e) {
+          const int j = db * EPD + e;
+          part[j & 3] += s_cur[j >> 4][j & 15];
+          mt = fmax_nan(mt, s_nxt[j >> 4][j & 15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // keep the PV MFMAs, the sums and the max in this section: without uses here the compiler
+      // sinks them past the select below, which it turns into a branch
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(oacc[db]));
+      lsum += (part[0] + part[1]) + (part[2] + part[3]);
+      asm volatile("" : "+v"(lsum));
+      mt = half_swap_max(mt) * sl;
+      float m_nx = (mt > m_used + kRescaleThresholdFp8) ? mt : m_used;
+      float a_nx = (m_nx == m_used) ? 1.f : fast_exp2(m_used - m_nx);
       asm volatile("" : "+v"(m_nx), "+v"(a_nx));
-      m_used = has1 ? m_nx : m_used;
       alpha = has1 ? a_nx : alpha;
+      m_used = has1 ? m_nx : m_used;
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_dma();
