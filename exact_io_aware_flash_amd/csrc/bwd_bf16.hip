@@ -172,38 +172,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   // for the key tail and the causal diagonal; interior tiles run without them.  Every MFMA
   // operand is loaded before the MFMAs that use it (the scheduling groups keep the compiler from
   // sinking the LDS reads next to their uses, where their latency would stall the MFMA pipe).
+  // S = Q K^T and dP = dO V^T of query part s; register r of half h holds query
+  // 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated in VGPRs by inline-asm MFMAs: this
+  // kernel's compiled MFMAs accumulate in AGPRs (its dK / dV accumulators need them), where every
+  // VALU read of S or dP would cost a v_accvgpr_read.  Operand reads run two MFMA pairs ahead of
+  // their use; `hook(c)` runs after MFMA pair c, in the same fenced slot (independent VALU work).
+  // The asm is opaque to the compiler's hazard tracking: a VALU read of S or dP needs 14 wait
+  // states after the MFMA that wrote it (gfx950), which callers provide.
+  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, auto hook)
+      __attribute__((always_inline)) {
+    bf16x8 qa[DC], oa[DC];
+    auto rd = [&](int c) {
+      qa[c] = lds_b128(tq + raddr[c] + 32 * s * D * 2);
+      oa[c] = lds_b128(to + raddr[c] + 32 * s * D * 2);
+    };
+    rd(0);
+    rd(1);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      if (c + 2 < DC) rd(c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c == 0) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(oa[0]), "v"(vreg[0]));
+      } else {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(oa[c]), "v"(vreg[c]));
+      }
+      hook(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no_hook = [](int) {};
+
   auto half = [&](auto maskc, const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
     constexpr bool MASK = decltype(maskc)::value;
-    // S = Q K^T and dP = dO V^T; register r of half h holds query qs + acc_row(r, h), key `key`.
-    // Accumulated in VGPRs by inline-asm MFMAs: this kernel's compiled MFMAs accumulate in AGPRs
-    // (its dK / dV accumulators need them), where every VALU read of S or dP below would cost a
-    // v_accvgpr_read.  The asm is opaque to the compiler's hazard tracking, so the wait states an
-    // MFMA result needs before a VALU instruction reads it (14 on gfx950) are issued explicitly.
-    // Operand reads run two MFMA pairs ahead of their use (fenced, so they stay there).
     f32x16 sacc, pacc;
-    {
-      bf16x8 qa[DC], oa[DC];
-      auto rd = [&](int c) {
-        qa[c] = lds_b128(tq + raddr[c] + 32 * s * D * 2);
-        oa[c] = lds_b128(to + raddr[c] + 32 * s * D * 2);
-      };
-      rd(0);
-      rd(1);
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        if (c + 2 < DC) rd(c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c == 0) {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(oa[0]), "v"(vreg[0]));
-        } else {
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(oa[c]), "v"(vreg[c]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
-    }
+    sp_chain(tq, to, s, sacc, pacc, no_hook);
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
     // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
     bf16x8 pp[2], dsp[2];
 #pragma unroll
@@ -248,6 +254,91 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
+  // dV += P^T dO ; dK += dS^T Q for query part s (as in `half`)
+  auto dvdk_part = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const bf16x8(&dsp)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int roff = (32 * s + 16 * mm) * D * 2;
+        dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
+                           dvacc[db]);
+        dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
+                           dkacc[db]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  };
+
+  // Interior tiles (no element mask), software-pipelined over the tile's NH query parts: the
+  // S / dP MFMAs of part s+1 run with the exponentials and dS of part s in their slots (one wave
+  // per SIMD: VALU work can only hide in this wave's own MFMA shadow), then the dV / dK MFMAs of
+  // part s.  S / dP of part s were written a whole dV / dK section earlier (or, for part 0,
+  // before explicit wait states), so the VALU reads need no further waits.
+  auto tile_pipelined = [&](const char* tq, const char* to, const float* Ls, const float* Ds)
+      __attribute__((always_inline)) {
+    f32x16 sa[2], pa[2];
+    sp_chain(tq, to, 0, sa[0], pa[0], no_hook);
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sa[0]), "+v"(pa[0]));  // 16 wait states
+#pragma unroll
+    for (int s = 0; s < NH; ++s) {
+      const int cur = s & 1;
+      bf16x8 pp[2], dsp[2];
+      float p[16];
+      // element r: query 32 s + 16 (r / 8) + 8 h + r % 8 of the tile.  Pair j = (2j, 2j+1) reads
+      // its LSE and D one pair ahead, takes its exponentials in slot 2j and its dS and bf16
+      // conversions in slot 2j+1.
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      f32x2 l2s[8], d2s[8];
+      auto rdld = [&](int j) {
+        const int row = 32 * s + 16 * (j >> 2) + 8 * h + 2 * (j & 3);
+        l2s[j] = *reinterpret_cast<const f32x2*>(Ls + row);
+        d2s[j] = *reinterpret_cast<const f32x2*>(Ds + row);
+      };
+      rdld(0);
+      auto valu_slot = [&](int i) {
+        const int j = i >> 1, r0 = 2 * j;
+        if ((i & 1) == 0) {
+          if (j + 1 < 8) {
+            rdld(j + 1);
+            asm volatile("" : "+v"(l2s[j + 1]), "+v"(d2s[j + 1]));  // issued in this slot
+          }
+          p[r0] = fast_exp2(__builtin_fmaf(sa[cur][r0], sl, -l2s[j][0]));
+          p[r0 + 1] = fast_exp2(__builtin_fmaf(sa[cur][r0 + 1], sl, -l2s[j][1]));
+          // computed in this slot (without a use here the compiler moves the work past the MFMAs)
+          asm volatile("" : "+v"(p[r0]), "+v"(p[r0 + 1]));
+        } else {
+          pp[r0 >> 3][r0 & 7] = (__bf16)p[r0];
+          pp[r0 >> 3][(r0 & 7) + 1] = (__bf16)p[r0 + 1];
+          dsp[r0 >> 3][r0 & 7] = (__bf16)(p[r0] * (pa[cur][r0] - d2s[j][0]));
+          dsp[r0 >> 3][(r0 & 7) + 1] = (__bf16)(p[r0 + 1] * (pa[cur][r0 + 1] - d2s[j][1]));
+          asm volatile("" : "+v"(pp[r0 >> 3]), "+v"(dsp[r0 >> 3]));
+        }
+      };
+      if (s + 1 < NH) {
+        constexpr int SPC = 16 / DC;  // VALU slots per MFMA pair
+        sp_chain(tq, to, s + 1, sa[cur ^ 1], pa[cur ^ 1], [&](int c) {
+#pragma unroll
+          for (int k = 0; k < SPC; ++k) valu_slot(SPC * c + k);
+        });
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) valu_slot(i);
+      }
+      // pin P / dS here, so that the conversions stay in the slots above
+      asm volatile("" : "+v"(pp[0]), "+v"(pp[1]), "+v"(dsp[0]), "+v"(dsp[1]));
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk_part(tq, to, s, pp, dsp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tq = par ? qbuf1 : qbuf0;
@@ -267,13 +358,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     // (d = 64 runs one body for every tile: a second copy costs it its second wave per SIMD)
     const bool tile_mask = (D == 64) || (k0 + BKV > N) || (CAUSAL && q0 < k0 + BKV - 1);
     if (!tile_mask) {
-#pragma unroll
-      for (int s = 0; s < NH; ++s) {
-        half(std::false_type{}, tq, to, Ls, Ds, s, q0 + 32 * s);
-        // keep the parts apart: hoisting the next part's operand reads over this one only
-        // raises register pressure (one wave per SIMD hides nothing with it)
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      tile_pipelined(tq, to, Ls, Ds);
     } else {
 #pragma unroll
       for (int s = 0; s < NH; ++s) {
