@@ -1,0 +1,86 @@
+"""Host-side logic of bench.py (no GPU needed): the one-GPU guard, kernel labels, and the counter
+summaries built from rocprofv3 CSV files (synthetic rows here, with known answers)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    sys.path.insert(0, ROOT)
+    import bench as b
+    return b
+
+
+def test_more_than_one_gpu_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_kernel_labels(bench):
+    lab = bench.kernel_label
+    assert lab("void fa::(anonymous namespace)::fwd_bf16_kernel<128, true, false, false>(fa::FwdArgs, fa::Sched)") == "fwd"
+    assert lab("void fa::(anonymous namespace)::fwd_bf16_kernel<64, false, true, false>(fa::FwdArgs, fa::Sched)") == \
+        "fwd_noncausal"
+    assert lab("void fa::(anonymous namespace)::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs, fa::Sched)") == "bwd_dkdv"
+    assert lab("void fa::(anonymous namespace)::fwd_mxfp8_kernel<128, true, false>(fa::Fp8FwdArgs, fa::Sched)") == \
+        "fwd_mxfp8"
+    assert lab("_ZN2fa12_GLOBAL__N_121mx_quantize_vt_kernelILi128EEEvPKDF16bPhS4_ii") == "mxfp8_quantize_vt"
+    assert lab("__amd_rocclr_copyBuffer") is None
+
+
+def _write_counter_csv(path, rows):
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_traffic_from_scales_by_the_copy_calibration(bench, tmp_path, monkeypatch):
+    # a 256 MiB copy reads 128 MiB on FETCH_SIZE (factor 2) and 256 MiB on WRITE_SIZE (factor 1);
+    # the forward's counters in KiB scale by those factors; per-dispatch rows are summed
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm.json"))
+    fwd = "void fa::(anonymous namespace)::fwd_bf16_kernel<128, true, false, false>(fa::FwdArgs, fa::Sched)"
+    mib = 1024  # KiB
+    fetch = [{"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE",
+              "Counter_Value": 128 * mib},
+             {"Dispatch_Id": 2, "Kernel_Name": fwd, "Counter_Name": "FETCH_SIZE", "Counter_Value": 100 * mib},
+             {"Dispatch_Id": 2, "Kernel_Name": fwd, "Counter_Name": "FETCH_SIZE", "Counter_Value": 50 * mib}]
+    write = [{"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE",
+              "Counter_Value": 256 * mib},
+             {"Dispatch_Id": 2, "Kernel_Name": fwd, "Counter_Name": "WRITE_SIZE", "Counter_Value": 64 * mib}]
+    for r in fetch + write:
+        r.update(Start_Timestamp=0, End_Timestamp=1000)
+    _write_counter_csv(tmp_path / "f.csv", fetch)
+    _write_counter_csv(tmp_path / "w.csv", write)
+    bench.traffic_from(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), workload="long")
+    rec = json.load(open(tmp_path / "hbm.json"))
+    assert rec["fetch_size_factor"] == pytest.approx(2.0) and rec["write_size_factor"] == pytest.approx(1.0)
+    k = {e["kernel"]: e for e in rec["kernels"]}["fwd"]
+    assert k["fetch_bytes_per_launch"] == pytest.approx(2 * 150 * 2 ** 20)
+    assert k["write_bytes_per_launch"] == pytest.approx(64 * 2 ** 20)
+    assert rec["csrc_sha256"] == bench.csrc_digest()
+
+
+def test_mfma_from_busy_fraction(bench, tmp_path):
+    # 1024 SIMDs x 1000 cycles per XCD (GRBM_GUI_ACTIVE is summed over 8 XCDs) with 512000 busy
+    # cycles is 50% busy; 1000 cycles per XCD over 500 ns is a 2 GHz clock
+    dkdv = "void fa::(anonymous namespace)::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs, fa::Sched)"
+    rows = []
+    for name, val in (("SQ_VALU_MFMA_BUSY_CYCLES", 512000), ("GRBM_GUI_ACTIVE", 8000), ("SQ_INSTS_MFMA", 16000)):
+        rows.append({"Dispatch_Id": 5, "Kernel_Name": dkdv, "Counter_Name": name, "Counter_Value": val,
+                     "Start_Timestamp": 0, "End_Timestamp": 500})
+    _write_counter_csv(tmp_path / "m.csv", rows)
+    table = bench.mfma_from(str(tmp_path / "m.csv"))
+    line = [l for l in table.splitlines() if l.startswith("| bwd_dkdv")][0]
+    assert "50.0%" in line and "2.00 GHz" in line
