@@ -9,9 +9,11 @@
 //
 // Three kernels on one stream:
 //  1. bwd_delta:  D per row (bandwidth-bound, 16-byte loads, shuffle reduction).
-//  2. bwd_dkdv:   one workgroup per (b*h, 128-key block): 4 waves x 32 keys.  K and V of the
-//                 wave's keys stay in registers as MFMA B operands; Q and dO tiles of 64 rows are
-//                 copied global -> LDS asynchronously (double-buffered), LSE and D beside them.
+//  2. bwd_dkdv:   one workgroup per (b*h, 128-key block).  d = 128: 8 waves, two per 32 keys
+//                 (one computes P and dV with K in registers, the other dP, dS and dK with V in
+//                 registers, P passing between them through LDS); d = 64: 4 waves, one per 32
+//                 keys, two workgroups per CU.  Q and dO tiles of 128 rows are copied
+//                 global -> LDS asynchronously (double-buffered), LSE and D beside them.
 //                 S = Q K^T puts one key per lane and 16 queries in registers, the A-operand
 //                 shape of dV = P^T dO and dK = dS^T Q; their B operands (dO and Q with queries as
 //                 the contraction index) are read from the same tiles with transposing reads.
@@ -52,9 +54,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
   if (row < rows && part == 0) delta[row] = acc;
 }
 
-// ------------------------------------------------------------------------------------- dK, dV
+// --------------------------------------------------------------------------- dK, dV at d = 64
+// One workgroup of 4 waves per (b*h, 128-key block), each wave doing all the work on 32 keys
+// (K and V both in registers); two workgroups fit on a CU, so each SIMD still runs two waves.
+// Short per-block tile lists (small N, block-sparse masks) favour this form over the paired
+// waves below, whose phase pipeline has a fill and a drain per workgroup.
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched sc) {
+  static_assert(D == 64, "the single-wave dK/dV kernel serves d = 64");
   constexpr int BKV = 128, BQ = 128;  // one mask block of keys against one of queries per step
   constexpr int NH = BQ / 32;          // 32-query parts of a query tile
   constexpr int DC = D / 16, DB = D / 32;
@@ -168,18 +175,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   wait_dma();
   __syncthreads();
 
-  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..).  MASK: element masks
-  // for the key tail and the causal diagonal; interior tiles run without them.  Every MFMA
-  // operand is loaded before the MFMAs that use it (the scheduling groups keep the compiler from
-  // sinking the LDS reads next to their uses, where their latency would stall the MFMA pipe).
-  // S = Q K^T and dP = dO V^T of query part s; register r of half h holds query
-  // 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated in VGPRs by inline-asm MFMAs: this
-  // kernel's compiled MFMAs accumulate in AGPRs (its dK / dV accumulators need them), where every
-  // VALU read of S or dP would cost a v_accvgpr_read.  Operand reads run two MFMA pairs ahead of
-  // their use; `hook(c)` runs after MFMA pair c, in the same fenced slot (independent VALU work).
-  // The asm is opaque to the compiler's hazard tracking: a VALU read of S or dP needs 14 wait
-  // states after the MFMA that wrote it (gfx950), which callers provide.
-  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, auto hook)
+  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..), with the element
+  // masks for the key tail and the causal diagonal.  S = Q K^T and dP = dO V^T of query part s:
+  // register r of half h holds query 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated in
+  // VGPRs by inline-asm MFMAs (the compiler's MFMAs may keep their accumulators in AGPRs, where
+  // each VALU read would cost a copy), operand reads two MFMA pairs ahead of their use.  The asm
+  // is opaque to the compiler's hazard tracking: a VALU read of S or dP needs 14 wait states
+  // after the MFMA that wrote it (gfx950), given after the chain.
+  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc)
       __attribute__((always_inline)) {
     bf16x8 qa[DC], oa[DC];
     auto rd = [&](int c) {
@@ -199,16 +202,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(oa[c]), "v"(vreg[c]));
       }
-      hook(c);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto no_hook = [](int) {};
 
-  auto half = [&](auto maskc, const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
-    constexpr bool MASK = decltype(maskc)::value;
+  auto half = [&](const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
     f32x16 sacc, pacc;
-    sp_chain(tq, to, s, sacc, pacc, no_hook);
+    sp_chain(tq, to, s, sacc, pacc);
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
     // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
     bf16x8 pp[2], dsp[2];
@@ -224,10 +224,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
         const float lv = e < 4 ? l0[e] : l1[e - 4];
         const float dv = e < 4 ? d0[e] : d1[e - 4];
         float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
-        if (MASK) {
-          const int qi = qs + 16 * mm + 8 * h + e;
-          if (key >= N || (CAUSAL && key > qi)) p = 0.f;
-        }
+        const int qi = qs + 16 * mm + 8 * h + e;
+        if (key >= N || (CAUSAL && key > qi)) p = 0.f;
         pp[mm][e] = (__bf16)p;
         dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
       }
@@ -254,91 +252,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
-  // dV += P^T dO ; dK += dS^T Q for query part s (as in `half`)
-  auto dvdk_part = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const bf16x8(&dsp)[2])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int roff = (32 * s + 16 * mm) * D * 2;
-        dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
-                           dvacc[db]);
-        dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
-                           dkacc[db]);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-    for (int i = 0; i < 4 * DB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-  };
-
-  // Interior tiles (no element mask), software-pipelined over the tile's NH query parts: the
-  // S / dP MFMAs of part s+1 run with the exponentials and dS of part s in their slots (one wave
-  // per SIMD: VALU work can only hide in this wave's own MFMA shadow), then the dV / dK MFMAs of
-  // part s.  S / dP of part s were written a whole dV / dK section earlier (or, for part 0,
-  // before explicit wait states), so the VALU reads need no further waits.
-  auto tile_pipelined = [&](const char* tq, const char* to, const float* Ls, const float* Ds)
-      __attribute__((always_inline)) {
-    f32x16 sa[2], pa[2];
-    sp_chain(tq, to, 0, sa[0], pa[0], no_hook);
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sa[0]), "+v"(pa[0]));  // 16 wait states
-#pragma unroll
-    for (int s = 0; s < NH; ++s) {
-      const int cur = s & 1;
-      bf16x8 pp[2], dsp[2];
-      float p[16];
-      // element r: query 32 s + 16 (r / 8) + 8 h + r % 8 of the tile.  Pair j = (2j, 2j+1) reads
-      // its LSE and D one pair ahead, takes its exponentials in slot 2j and its dS and bf16
-      // conversions in slot 2j+1.
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-      f32x2 l2s[8], d2s[8];
-      auto rdld = [&](int j) {
-        const int row = 32 * s + 16 * (j >> 2) + 8 * h + 2 * (j & 3);
-        l2s[j] = *reinterpret_cast<const f32x2*>(Ls + row);
-        d2s[j] = *reinterpret_cast<const f32x2*>(Ds + row);
-      };
-      rdld(0);
-      auto valu_slot = [&](int i) {
-        const int j = i >> 1, r0 = 2 * j;
-        if ((i & 1) == 0) {
-          if (j + 1 < 8) {
-            rdld(j + 1);
-            asm volatile("" : "+v"(l2s[j + 1]), "+v"(d2s[j + 1]));  // issued in this slot
-          }
-          p[r0] = fast_exp2(__builtin_fmaf(sa[cur][r0], sl, -l2s[j][0]));
-          p[r0 + 1] = fast_exp2(__builtin_fmaf(sa[cur][r0 + 1], sl, -l2s[j][1]));
-          // computed in this slot (without a use here the compiler moves the work past the MFMAs)
-          asm volatile("" : "+v"(p[r0]), "+v"(p[r0 + 1]));
-        } else {
-          pp[r0 >> 3][r0 & 7] = (__bf16)p[r0];
-          pp[r0 >> 3][(r0 & 7) + 1] = (__bf16)p[r0 + 1];
-          dsp[r0 >> 3][r0 & 7] = (__bf16)(p[r0] * (pa[cur][r0] - d2s[j][0]));
-          dsp[r0 >> 3][(r0 & 7) + 1] = (__bf16)(p[r0 + 1] * (pa[cur][r0 + 1] - d2s[j][1]));
-          asm volatile("" : "+v"(pp[r0 >> 3]), "+v"(dsp[r0 >> 3]));
-        }
-      };
-      if (s + 1 < NH) {
-        constexpr int SPC = 16 / DC;  // VALU slots per MFMA pair
-        sp_chain(tq, to, s + 1, sa[cur ^ 1], pa[cur ^ 1], [&](int c) {
-#pragma unroll
-          for (int k = 0; k < SPC; ++k) valu_slot(SPC * c + k);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) valu_slot(i);
-      }
-      // pin P / dS here, so that the conversions stay in the slots above
-      asm volatile("" : "+v"(pp[0]), "+v"(pp[1]), "+v"(dsp[0]), "+v"(dsp[1]));
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk_part(tq, to, s, pp, dsp);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tq = par ? qbuf1 : qbuf0;
@@ -353,20 +266,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
     }
     const float* Ls = lbuf[par];
     const float* Ds = dbuf[par];
-    // tiles touching the causal diagonal or the key tail take the masked path; queries past N
-    // need no mask (their LSE is +inf, so P = 0)
-    // (d = 64 runs one body for every tile: a second copy costs it its second wave per SIMD)
-    const bool tile_mask = (D == 64) || (k0 + BKV > N) || (CAUSAL && q0 < k0 + BKV - 1);
-    if (!tile_mask) {
-      tile_pipelined(tq, to, Ls, Ds);
-    } else {
+    // one body (with the element masks) for every tile: a second copy would cost the kernel its
+    // second workgroup per CU; queries past N need no mask (their LSE is +inf, so P = 0)
 #pragma unroll
-      for (int s = 0; s < NH; ++s) {
-        const int qs = q0 + 32 * s;
-        if (qs >= N) continue;
-        if (CAUSAL && qs + 31 < k0w) continue;  // every query of this half precedes every key of the wave
-        half(std::true_type{}, tq, to, Ls, Ds, s, qs);
-      }
+    for (int s = 0; s < NH; ++s) {
+      const int qs = q0 + 32 * s;
+      if (qs >= N) continue;
+      if (CAUSAL && qs + 31 < k0w) continue;  // every query of this half precedes every key of the wave
+      half(tq, to, Ls, Ds, s, qs);
     }
     if (has_next) rowstats_store(par ^ 1);
     wait_dma();
@@ -390,6 +297,421 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
         a.dv[off] = (__bf16)dvacc[db][r];
         a.dk[off] = (__bf16)(dkacc[db][r] * scale);
       }
+    }
+}
+
+// ------------------------------------------------------------------------------------- dK, dV
+// One workgroup of 8 waves per (b*h, 128-key block).  Waves w and w + 4 own the same 32 keys
+// k0 + 32 (w % 4) .. + 31 and split the work on them (two waves per SIMD, so each one's LDS and
+// VALU latency has the other's MFMAs to hide behind):
+//   P wave  (w < 4):  S = Q K^T, P = exp(S - LSE) with the masks, dV += P^T dO   (K in registers)
+//   dS wave (w >= 4): dP = dO V^T, dS = P (dP - D), dK += dS^T Q              (V in registers)
+// P goes from one to the other through LDS as bf16, the values dV uses.  Query tiles of 128 rows
+// are split into four 32-query parts; the dS wave runs one part behind: in phase s of tile t the
+// P waves handle part s and the dS waves part s - 1 (in phase 0, part 3 of tile t - 1), with one
+// barrier per phase.  Q and dO tiles are double-buffered; the copy of tile t + 1 starts in
+// phase 1 of tile t, once the dS waves are done with tile t - 1.
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
+  constexpr int BKV = 128, BQ = 128;  // one mask block of keys against one of queries per tile
+  constexpr int NH = BQ / 32;          // 32-query parts of a query tile
+  constexpr int DC = D / 16, DB = D / 32;
+  using QT = DmaTile<BQ, D, 8>;  // Q or dO rows (read row-wise and transposed)
+
+  __shared__ __attribute__((aligned(1024))) char qbuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char pbuf[4][2][2048];  // P of one part, per key group and phase parity
+  __shared__ __attribute__((aligned(16))) float lbuf[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];
+  __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int bcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w & 3;     // key group: keys k0 + 32 grp ..
+  const bool dsw = w >= 4;   // dS wave
+  const int N = a.N;
+  int bh, kt;
+  sched_decode(sc, gridDim.x, bh, kt);
+  const int k0 = kt * BKV;
+  const int k0w = k0 + 32 * grp;
+  const size_t base = (size_t)bh * N * D;
+  const size_t rbase = (size_t)bh * N;
+  const __bf16* __restrict__ Qh = a.q + base;
+  const __bf16* __restrict__ Oh = a.dout + base;
+
+  // ---- query tiles (of BQ rows) that see this key block
+  const int nqt = (N + BQ - 1) / BQ;
+  int q_first = 0, ntiles = nqt;
+  if (CAUSAL) {
+    q_first = k0 / BQ;
+    ntiles = nqt - q_first;
+  }
+  if (SPARSE) {
+    if (w == 0) {
+      const int cnt = build_block_list(a.mask, a.nb, kt, true, CAUSAL ? kt : 0, a.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    ntiles = bcount;  // one query tile per mask block
+  }
+  auto tile_start = [&](int t) -> int {
+    if (SPARSE) return (int)blist[t] * kMaskBlock;
+    return (q_first + t) * BQ;
+  };
+
+  // ---- this lane's key: its K (P wave) or V (dS wave) row as B operands (features 16c + 8h ..)
+  const int key = k0w + c32;
+  const __bf16* __restrict__ kvsrc = (dsw ? a.v : a.k) + base;
+  bf16x8 kv[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+    kv[c] = key < N ? *reinterpret_cast<const bf16x8*>(kvsrc + (size_t)key * D + 16 * c + 8 * h) : zero_bf16x8();
+  f32x16 acc[DB];  // dV (P wave) or dK / scale (dS wave)
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = zero16();
+  const float sl = a.scale_log2;
+
+  // ---- per-lane LDS addresses
+  // A operands (Q, dO rows): row 32 s + perm32(c32) (32 s added per use), features 16c + 8h ..
+  int raddr[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) raddr[c] = QT::off(perm32(c32), 16 * c + 8 * h);
+  // B operands (dO^T, Q^T: queries as the contraction index), transposed read u of feature
+  // block db: lane j of its 16-lane group addresses query row 8h + 4u + j/4 (+ 32 s + 16 mm)
+  int taddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) taddr[u][db] = QT::off4(8 * h + 4 * u + (j >> 2), 32 * db + 16 * g + 4 * (j & 3));
+  }
+
+  QT qdma, odma;
+  qdma.init(w, lane);
+  odma.init(w, lane);
+  // LSE and D of the next tile: loaded when its copy starts, used only when stored (at the end
+  // of the tile), so that no wait on the loads holds up the copies issued before them
+  float lraw = 0.f, draw = 0.f;
+  auto rowstats_load = [&](int q0) {
+    if (tid < BQ) {
+      const int qr = q0 + tid;
+      lraw = qr < N ? a.lse[rbase + qr] : neg_inf();
+      draw = qr < N ? a.delta[rbase + qr] : 0.f;
+    }
+  };
+  auto rowstats_store = [&](int buf) {
+    if (tid < BQ) {
+      // rows past N, or rows that see no key, get +inf so that P = 0
+      lbuf[buf][tid] = (lraw == neg_inf()) ? __builtin_huge_valf() : lraw * kLog2e;
+      dbuf[buf][tid] = draw;
+    }
+  };
+
+  if (ntiles > 0) {
+    const int q0 = tile_start(0);
+    qdma.issue(Qh, N, qbuf0, q0, w);
+    odma.issue(Oh, N, obuf0, q0, w);
+    rowstats_load(q0);
+    wait_dma();
+    rowstats_store(0);
+  }
+  __syncthreads();
+
+  // X B^T for query part s, X rows read from tile `t` (Q or dO), B = this wave's K or V rows:
+  // register r of half h holds query 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated
+  // in VGPRs by inline-asm MFMAs (the compiler's MFMAs may keep their accumulators in AGPRs,
+  // where each VALU read would cost a copy).  Operand reads run two MFMAs ahead; `hook(c)` runs
+  // after MFMA c in the same fenced slot (independent VALU work, issued while the MFMA runs).
+  // The accumulator starts at zero, or (`cinit`) at a per-row vector read from LDS (the dS
+  // waves start dP at -D), or (`mask`) at -inf where the pair (query, key) is masked (the key
+  // tail, and the causal diagonal for query block row qs), so that P = exp(S - LSE) is 0 there
+  // without further VALU work.  The asm is opaque to the compiler's hazard tracking: a VALU read
+  // of the result needs 14 wait states after the last MFMA (gfx950), given at the end, and an
+  // MFMA reading a VALU result as its accumulator needs 2, given before it.
+  auto chain = [&](const char* t, int s, f32x16& x, bool mask, int qs, const float* cinit, auto hook)
+      __attribute__((always_inline)) {
+    bf16x8 op[DC];
+    auto rd = [&](int c) { op[c] = lds_b128(t + raddr[c] + 32 * s * D * 2); };
+    rd(0);
+    rd(1);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      if (c + 2 < DC) rd(c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c == 0) {
+        if (cinit) {
+          // accumulator initialised from LDS: 16 rows 16 (r / 8) + 8h + r % 8 of a row vector
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(cinit + 16 * (i >> 1) + 8 * h + 4 * (i & 1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 * i + j] = v[j];
+          }
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(x) : "v"(op[0]), "v"(kv[0]));
+        } else if (mask) {
+          // element r is query qs + 8h + 16 (r / 8) + r % 8: masked when 16 (r / 8) + r % 8 < thr
+          const int thr = key >= N ? 32 : (CAUSAL ? key - qs - 8 * h : 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = 16 * (r >> 3) + (r & 7) < thr ? neg_inf() : 0.f;
+          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(x) : "v"(op[0]), "v"(kv[0]));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(x) : "v"(op[0]), "v"(kv[0]));
+        }
+      } else {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(x) : "v"(op[c]), "v"(kv[c]));
+      }
+      hook(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x));  // 16 wait states
+  };
+
+  // acc += X^T Y for query part s: X = P or dS of the part (A operands, one key per lane and
+  // queries 16 mm + 8h .. as the contraction index), Y = dO or Q rows of the part, read from
+  // tile `t` with transposing reads (two 8-byte reads per MFMA, kept four MFMAs ahead); MFMAs
+  // on the same accumulator DB apart (a region of its own, so that its scheduling groups take
+  // only its own reads)
+  auto accumulate = [&](const char* t, int s, const bf16x8(&x)[2]) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int roff = (32 * s + 16 * mm) * D * 2;
+        acc[db] = mfma32(x[mm], join8(lds_tr4(t + roff + taddr[0][db]), lds_tr4(t + roff + taddr[1][db])), acc[db]);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // copy of tile t + 1 into the other buffers (from phase 2 of tile t, once no wave reads tile
+  // t - 1 any more), by all waves
+  auto prefetch = [&](int t, int buf) {
+    const int qn = tile_start(t + 1);
+    qdma.issue(Qh, N, buf ? qbuf1 : qbuf0, qn, w);
+    odma.issue(Oh, N, buf ? obuf1 : obuf0, qn, w);
+    rowstats_load(qn);
+  };
+  // end of tile t: the next tile's LSE and D stored, its copies landed (a barrier follows)
+  auto finish_tile = [&](bool has_next, int buf) {
+    if (has_next) rowstats_store(buf);
+    wait_dma();
+  };
+  auto tile_mask = [&](int q0) -> bool {
+    // tiles touching the key tail or the causal diagonal; queries past N need no mask (their
+    // LSE is +inf, so P = 0)
+    return (k0 + BKV > N) || (CAUSAL && q0 < k0 + BKV - 1);
+  };
+
+  // Parts are never skipped: the masks give P = 0 wherever a part sees no key (and rows past N
+  // have P = 0 through their LSE), and the phase barrier would keep the group waiting anyway.
+  //
+  // Number the 32-query parts g = 4 t + s over the tiles.  In phase g (one barrier each):
+  //   P wave:  S MFMAs of part g, with the exponentials of part g - 1 in their slots; P of part
+  //            g - 1 to LDS; dV MFMAs of part g - 1
+  //   dS wave: dP MFMAs of part g - 1, with dS of part g - 2 (P of g - 2 from LDS) in their
+  //            slots; dK MFMAs of part g - 2
+  // Tile t - 1 is last read in phase 1 of tile t (dK of its part 3), so the copy of tile t + 1
+  // into its buffers starts in phase 2.  After the last tile, one more phase with a barrier
+  // (P wave: exponentials and dV of the last part) and one without (dS wave: its last part).
+  // Pairs j = 0..7 (elements 2j, 2j + 1) of a part's scores take chain slots SKIP .. DC - 1: the
+  // first slots give the LDS reads the pairs need (P, the row statistics) time to land.
+  constexpr int SKIP = DC / 4;
+  auto pair_slot = [](int j) constexpr { return SKIP + j * (DC - SKIP) / 8; };
+  // Row statistics (LSE or D) of a part reach the lanes through one 4-byte LDS read per lane: lane
+  // 16 i + k holds the value of row 16 (k / 8) + 8 (i / 2) + k % 8 of the part, and a DPP row
+  // broadcast of lane k within each row of 16 lanes then gives every lane of half h the value of
+  // score element r = k (row 16 (r / 8) + 8h + r % 8).
+  auto stat_load = [&](const float* rows, int s) -> float {
+    return rows[32 * s + 16 * ((lane & 15) >> 3) + 8 * h + (lane & 7)];
+  };
+  auto stat_of = [](float v, int r) __attribute__((always_inline)) -> float { return row_bcast(v, r); };
+  if (!dsw) {
+    f32x16 sv[2];  // S of part g in sv[g & 1]
+    // phase with S of part s of tile buffers tq (when HS) and exponentials / dV of part s_e of
+    // buffers to_e (when HE)
+    auto p_phase = [&](auto hsc, auto hec, const char* tq, int s, bool mask, int qs, const char* to_e,
+                       const float* Ls, int s_e) __attribute__((always_inline)) {
+      constexpr bool HS = decltype(hsc)::value, HE = decltype(hec)::value;
+      bf16x8 pp[2];
+      float lr = 0.f;  // LSE of part s_e, one row per lane (see stat_of)
+      if (HE) lr = stat_load(Ls, s_e);
+      const f32x16& xe = sv[s_e & 1];
+      auto eslot = [&](int c) __attribute__((always_inline)) {
+        bool used[2] = {false, false};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (pair_slot(j) != c) continue;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int r = 2 * j + k;
+            pp[r >> 3][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(xe[r], sl, -stat_of(lr, r)));
+          }
+          used[j >> 2] = true;
+        }
+        // computed in this slot
+        if (used[0]) asm volatile("" : "+v"(pp[0]));
+        if (used[1]) asm volatile("" : "+v"(pp[1]));
+      };
+      if (HS)
+        chain(tq, s, sv[s & 1], mask, qs, nullptr, [&](int c) {
+          if (HE) eslot(c);
+        });
+      else if (HE) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) eslot(c);
+      }
+      if (HE) {
+        char* pb = pbuf[grp][s_e & 1];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) *reinterpret_cast<bf16x8*>(pb + 1024 * mm + 16 * lane) = pp[mm];
+        accumulate(to_e, s_e, pp);
+      }
+    };
+    auto p_step = [&](int t, auto parity, auto firstc) {
+      constexpr int par = decltype(parity)::value;
+      constexpr bool FIRST = decltype(firstc)::value;
+      const char* tq = par ? qbuf1 : qbuf0;
+      const char* to = par ? obuf1 : obuf0;
+      const int q0 = tile_start(t);
+      const bool has_next = t + 1 < ntiles;
+      const bool mask = tile_mask(q0);
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        if (s == 2 && has_next) prefetch(t, par ^ 1);
+        if (s > 0)
+          p_phase(std::true_type{}, std::true_type{}, tq, s, mask, q0 + 32 * s, to, lbuf[par], s - 1);
+        else if (!FIRST)
+          p_phase(std::true_type{}, std::true_type{}, tq, s, mask, q0, par ? obuf0 : obuf1, lbuf[par ^ 1], NH - 1);
+        else
+          p_phase(std::true_type{}, std::false_type{}, tq, s, mask, q0, to, lbuf[par], 0);
+        if (s == NH - 1) finish_tile(has_next, par ^ 1);
+        lds_barrier();
+      }
+    };
+    auto p_last = [&](auto parity) {  // parity of the last tile
+      constexpr int par = decltype(parity)::value;
+      p_phase(std::false_type{}, std::true_type{}, qbuf0, 0, false, 0, par ? obuf1 : obuf0, lbuf[par], NH - 1);
+      lds_barrier();
+    };
+    if (ntiles > 0) {
+      p_step(0, std::integral_constant<int, 0>{}, std::true_type{});
+      for (int t = 1; t < ntiles; t += 2) {
+        p_step(t, std::integral_constant<int, 1>{}, std::false_type{});
+        if (t + 1 < ntiles) p_step(t + 1, std::integral_constant<int, 0>{}, std::false_type{});
+      }
+      if ((ntiles - 1) & 1)
+        p_last(std::integral_constant<int, 1>{});
+      else
+        p_last(std::integral_constant<int, 0>{});
+    }
+  } else {
+    f32x16 dpv[2];  // dP of part g in dpv[g & 1]
+    // phase with dP of part s_p of buffers to_p (when HP) and dS / dK of part s_d of buffers
+    // tq_d (when HD)
+    auto ds_phase = [&](auto hpc, auto hdc, const char* to_p, int s_p, const char* tq_d, const float* Ds_d, int s_d)
+        __attribute__((always_inline)) {
+      constexpr bool HP = decltype(hpc)::value, HD = decltype(hdc)::value;
+      bf16x8 pv[2], dsp[2];
+      float dr = 0.f;  // D of part s_d, one row per lane (see stat_of)
+      if (HD) {
+        const char* pb = pbuf[grp][s_d & 1];
+        pv[0] = lds_b128(pb + 16 * lane);
+        pv[1] = lds_b128(pb + 1024 + 16 * lane);
+        dr = stat_load(Ds_d, s_d);
+      }
+      const f32x16& xd = dpv[s_d & 1];
+      auto dslot = [&](int c) __attribute__((always_inline)) {
+        bool used[2] = {false, false};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (pair_slot(j) != c) continue;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int r = 2 * j + k;
+            dsp[r >> 3][r & 7] = (__bf16)((float)pv[r >> 3][r & 7] * (xd[r] - stat_of(dr, r)));
+          }
+          used[j >> 2] = true;
+        }
+        // computed in this slot
+        if (used[0]) asm volatile("" : "+v"(dsp[0]));
+        if (used[1]) asm volatile("" : "+v"(dsp[1]));
+      };
+      if (HP)
+        chain(to_p, s_p, dpv[s_p & 1], false, 0, nullptr, [&](int c) {
+          if (HD) dslot(c);
+        });
+      else if (HD) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) dslot(c);
+      }
+      if (HD) accumulate(tq_d, s_d, dsp);
+    };
+    auto ds_step = [&](int t, auto parity, auto firstc) {
+      constexpr int par = decltype(parity)::value;
+      constexpr bool FIRST = decltype(firstc)::value;
+      const char* tq = par ? qbuf1 : qbuf0;
+      const char* to = par ? obuf1 : obuf0;
+      const char* tq_prev = par ? qbuf0 : qbuf1;
+      const char* to_prev = par ? obuf0 : obuf1;
+      const bool has_next = t + 1 < ntiles;
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        if (s == 2 && has_next) prefetch(t, par ^ 1);
+        if (s >= 2)
+          ds_phase(std::true_type{}, std::true_type{}, to, s - 1, tq, dbuf[par], s - 2);
+        else if (s == 1) {
+          if (FIRST)
+            ds_phase(std::true_type{}, std::false_type{}, to, 0, tq, dbuf[par], 0);
+          else
+            ds_phase(std::true_type{}, std::true_type{}, to, 0, tq_prev, dbuf[par ^ 1], NH - 1);
+        } else if (!FIRST) {
+          ds_phase(std::true_type{}, std::true_type{}, to_prev, NH - 1, tq_prev, dbuf[par ^ 1], NH - 2);
+        }
+        if (s == NH - 1) finish_tile(has_next, par ^ 1);
+        lds_barrier();
+      }
+    };
+    auto ds_last = [&](auto parity) {  // parity of the last tile
+      constexpr int par = decltype(parity)::value;
+      const char* tq = par ? qbuf1 : qbuf0;
+      const char* to = par ? obuf1 : obuf0;
+      ds_phase(std::true_type{}, std::true_type{}, to, NH - 1, tq, dbuf[par], NH - 2);
+      lds_barrier();
+      ds_phase(std::false_type{}, std::true_type{}, to, 0, tq, dbuf[par], NH - 1);
+    };
+    if (ntiles > 0) {
+      ds_step(0, std::integral_constant<int, 0>{}, std::true_type{});
+      for (int t = 1; t < ntiles; t += 2) {
+        ds_step(t, std::integral_constant<int, 1>{}, std::false_type{});
+        if (t + 1 < ntiles) ds_step(t + 1, std::integral_constant<int, 0>{}, std::false_type{});
+      }
+      if ((ntiles - 1) & 1)
+        ds_last(std::integral_constant<int, 1>{});
+      else
+        ds_last(std::integral_constant<int, 0>{});
+    }
+  }
+
+  // ---- epilogue: lane holds feature 32 db + c32 of keys k0w + 8 g + 4 h + e (register 4 g + e)
+  __bf16* __restrict__ dst = dsw ? a.dk : a.dv;
+  const float f = dsw ? a.scale : 1.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = k0w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (kr < N) dst[base + (size_t)kr * D + 32 * db + c32] = (__bf16)(acc[db][r] * f);
     }
 }
 
@@ -576,9 +898,15 @@ hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
 template <int D, bool C, bool S>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int nkv = (a.N + 127) / 128;
-  static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, C, S>));
-  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc);
+  if constexpr (D == 64) {
+    static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_wave_kernel<D, C, S>), 256);
+    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+    hipLaunchKernelGGL((bwd_dkdv_wave_kernel<D, C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc);
+  } else {
+    static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, C, S>), 512);
+    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, C, S>), dim3(nkv * a.BH), dim3(512), 0, st, a, sc);
+  }
   return hipGetLastError();
 }
 

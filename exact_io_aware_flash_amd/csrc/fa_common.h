@@ -99,6 +99,9 @@ __device__ __forceinline__ void dma16(const Rsrc& r, void* lds_block, int voff, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds_block, 16, voff, soff, 0, 0);
 }  // soff stays 0 in this library: the range check does not cover it
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// workgroup barrier that waits for this wave's LDS operations only (copies into LDS still in
+// flight stay in flight), and that the compiler moves no memory access across
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // wait until at most N of this wave's vector-memory instructions (copies included) are in
 // flight; they complete in issue order, so everything issued before the last N has landed
 template <int N>
@@ -170,6 +173,34 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// DPP row broadcast (gfx90a and later): every lane receives the value of lane k of its own row of
+// 16 lanes.  k must be a constant after inlining and unrolling (the switch then folds away).
+template <int K>
+__device__ __forceinline__ float row_bcast_k(float v) {
+  static_assert(K >= 0 && K < 16, "lane within a row of 16");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_bcast(float v, int k) {
+  switch (k) {
+    case 0: return row_bcast_k<0>(v);
+    case 1: return row_bcast_k<1>(v);
+    case 2: return row_bcast_k<2>(v);
+    case 3: return row_bcast_k<3>(v);
+    case 4: return row_bcast_k<4>(v);
+    case 5: return row_bcast_k<5>(v);
+    case 6: return row_bcast_k<6>(v);
+    case 7: return row_bcast_k<7>(v);
+    case 8: return row_bcast_k<8>(v);
+    case 9: return row_bcast_k<9>(v);
+    case 10: return row_bcast_k<10>(v);
+    case 11: return row_bcast_k<11>(v);
+    case 12: return row_bcast_k<12>(v);
+    case 13: return row_bcast_k<13>(v);
+    case 14: return row_bcast_k<14>(v);
+    default: return row_bcast_k<15>(v);
+  }
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
