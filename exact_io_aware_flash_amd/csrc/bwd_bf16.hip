@@ -20,6 +20,8 @@
 //  3. bwd_dq:     one workgroup per (b*h, 128-query block), K and V tiles of 64 keys copied
 //                 asynchronously into LDS: S^T = K Q^T and dP^T = V dO^T give one query per lane
 //                 (the B-operand shape of dQ^T = K^T dS^T); K^T is read transposed from the K tile.
+//                 The tile's two 32-key blocks are software-pipelined (the exponentials and dS of
+//                 one block between the MFMAs of the other).
 // dQ is produced without atomics, so every output element is written once and results are
 // bitwise reproducible run to run.
 #include <type_traits>
@@ -804,6 +806,73 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
   wait_dma();
   __syncthreads();
 
+  // S^T = K Q^T and dP^T = V dO^T of key block kb of the tile: register r of half h holds key
+  // k0 + 32 kb + acc_row(r, h), query qrow.  Operand reads run two MFMA pairs ahead; `hook(c)`
+  // runs after MFMA pair c in the same fenced slot.  With `mask`, S^T starts at -inf on the
+  // masked pairs (key >= N, or after the query when causal), so that P = 0 there.
+  auto chain = [&](const char* tk, const char* tv, int kb, f32x16& sacc, f32x16& pacc, bool mask, int k0,
+                   auto hook) __attribute__((always_inline)) {
+    bf16x8 ka[DC], va[DC];
+    auto rd = [&](int c) {
+      ka[c] = lds_b128(tk + raddr[c] + 32 * kb * D * 2);
+      va[c] = lds_b128(tv + raddr[c] + 32 * kb * D * 2);
+    };
+    rd(0);
+    rd(1);
+    if (mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = k0 + 32 * kb + acc_row(r, h);
+        sacc[r] = (kr >= N || (CAUSAL && kr > qrow)) ? neg_inf() : 0.f;
+      }
+    } else {
+      sacc = zero16();
+    }
+    pacc = zero16();
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      if (c + 2 < DC) rd(c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      sacc = mfma32(ka[c], qreg[c], sacc);
+      pacc = mfma32(va[c], doreg[c], pacc);
+      hook(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // slot c of `slots`: P = exp(S - LSE) and dS = P (dP - D) of 16 / slots score elements, as
+  // bf16 B operands of dQ^T (dsp[m2] holds keys 16 m2 + 8h + 0..7 of the block)
+  auto ds_slot = [&](const f32x16& sv, const f32x16& pv, bf16x8(&dsp)[2], int c, int slots)
+      __attribute__((always_inline)) {
+    const int per = 16 / slots, m2 = (per * c) >> 3;
+#pragma unroll
+    for (int k = 0; k < per; ++k) {
+      const int r = per * c + k;
+      const float p = fast_exp2(__builtin_fmaf(sv[r], sl, -lse2));
+      dsp[m2][r & 7] = (__bf16)(p * (pv[r] - dval));
+    }
+    asm volatile("" : "+v"(dsp[m2]));  // computed in this slot
+  };
+  // dQ^T += K^T dS^T for key block kb (contraction over its 32 keys), K^T by transposing reads
+  // kept two MFMAs ahead; `hook(i)` runs after MFMA i in the same fenced slot
+  auto dq_mfmas = [&](const char* tk, int kb, const bf16x8(&dsp)[2], auto hook) __attribute__((always_inline)) {
+    s16x4 tr[2 * DB][2];
+    auto trd = [&](int i) {  // MFMA i: feature block i / 2, keys 16 (i % 2) ..
+      const int roff = (32 * kb + 16 * (i & 1)) * D * 2;
+      tr[i][0] = lds_tr4(tk + roff + taddr[0][i >> 1]);
+      tr[i][1] = lds_tr4(tk + roff + taddr[1][i >> 1]);
+    };
+    trd(0);
+    trd(1);
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      if (i + 2 < 2 * DB) trd(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dqacc[i >> 1] = mfma32(join8(tr[i][0], tr[i][1]), dsp[i & 1], dqacc[i >> 1]);
+      hook(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tk = par ? kbuf1 : kbuf0;
@@ -815,53 +884,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
       kdma.issue(Kh, N, par ? kbuf0 : kbuf1, kn, w);
       vdma.issue(Vh, N, par ? vbuf0 : vbuf1, kn, w);
     }
+    // tiles touching the key tail or the causal diagonal start S^T at -inf on masked pairs
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (CAUSAL && k0 + 32 * kb > q0 + 32 * w + 31) continue;  // every key of the block follows every query
-      // S^T = K Q^T, dP^T = V dO^T; register r of half h holds key k0 + 32 kb + acc_row(r, h), query qrow
-      f32x16 sacc = zero16(), pacc = zero16();
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        sacc = mfma32(lds_b128(tk + raddr[c] + 32 * kb * D * 2), qreg[c], sacc);
-        pacc = mfma32(lds_b128(tv + raddr[c] + 32 * kb * D * 2), doreg[c], pacc);
-      }
-      // operand reads run two MFMA pairs ahead of the MFMAs that consume them
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int c = 0; c < DC - 2; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      bf16x8 dsp[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lse2));
-        if (need_mask) {
-          const int kr = k0 + 32 * kb + acc_row(r, h);
-          if (kr >= N || (CAUSAL && kr > qrow)) p = 0.f;
-        }
-        dsp[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dval));
-      }
-      // dQ^T += K^T dS^T (contraction over the 32 keys; dsp[m2] holds keys 16 m2 + 8h + 0..7)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-          const int roff = (32 * kb + 16 * m2) * D * 2;
-          dqacc[db] = mfma32(join8(lds_tr4(tk + roff + taddr[0][db]), lds_tr4(tk + roff + taddr[1][db])), dsp[m2],
-                             dqacc[db]);
-        }
-      // each MFMA takes one transposed operand (two 8-byte transposing reads), kept two ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-      for (int i = 0; i < 2 * DB - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-    }
+    // The two 32-key blocks of the tile, software-pipelined: the S^T / dP^T MFMAs of block 1
+    // carry the exponentials and dS of block 0 in their slots, the dQ^T MFMAs of block 0 those
+    // of block 1 (VALU work issued while the wave's own MFMAs run).
+    f32x16 sa[2], pa[2];
+    bf16x8 dsp[2][2];
+    chain(tk, tv, 0, sa[0], pa[0], need_mask, k0, [](int) {});
+    chain(tk, tv, 1, sa[1], pa[1], need_mask, k0, [&](int c) { ds_slot(sa[0], pa[0], dsp[0], c, DC); });
+    dq_mfmas(tk, 0, dsp[0], [&](int i) { ds_slot(sa[1], pa[1], dsp[1], i, 2 * DB); });
+    dq_mfmas(tk, 1, dsp[1], [](int) {});
     wait_dma();
     __syncthreads();
   };

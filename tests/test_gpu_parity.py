@@ -111,21 +111,37 @@ def test_ragged_multi_tile(dev, d, causal):
     _run_and_compare(f"ragged dense N=1000 d={d}", t, 0.1, causal, dev, heads=[(0, 1), (1, 0)])
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_dead_rows(dev, dtype):
+def test_dead_rows(dev, dtype, d):
     """Rows that see no key: O = 0, LSE = -inf, no gradient (a zero mask row; and causal with a
     mask that only allows later blocks)."""
     N = 384
-    t = workloads.random_case(1, 2, N, 64, dtype, seed=400)
+    t = workloads.random_case(1, 2, N, d, dtype, seed=400 + d)
     t.block_mask = np.array([[1, 0, 0], [0, 0, 0], [1, 1, 1]], dtype=np.uint8)
-    res = _run_and_compare(f"dead rows {dtype}", t, 0.125, False, dev, heads=[(0, 0), (0, 1)])
+    res = _run_and_compare(f"dead rows {dtype} d={d}", t, 1.0 / math.sqrt(d), False, dev, heads=[(0, 0), (0, 1)])
     o = G.host_f64(res["o"])
     assert np.all(o[:, :, 128:256] == 0)
     assert np.all(np.isneginf(res["lse"][:, :, 128:256].cpu().numpy()))
     assert np.all(G.host_f64(res["dq"])[:, :, 128:256] == 0)
     t.block_mask = np.array([[0, 1, 1], [1, 0, 1], [1, 1, 1]], dtype=np.uint8)
-    res = _run_and_compare(f"dead rows causal {dtype}", t, 0.125, True, dev, heads=[(0, 0), (0, 1)])
+    res = _run_and_compare(f"dead rows causal {dtype} d={d}", t, 1.0 / math.sqrt(d), True, dev,
+                           heads=[(0, 0), (0, 1)])
     assert np.all(np.isneginf(res["lse"][:, :, 0:128].cpu().numpy()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_empty_key_block(dev, d, causal):
+    """A key block that no query block sees (an empty mask column): its workgroup has no query
+    tile at all, and dK, dV of its keys are exactly zero; the other blocks match the oracle."""
+    N = 3 * 128 - 40  # ragged last block
+    t = workloads.random_case(1, 2, N, d, "bf16", seed=450 + d)
+    t.block_mask = np.array([[1, 0, 0], [1, 0, 1], [1, 0, 1]], dtype=np.uint8)
+    res = _run_and_compare(f"empty key block d={d} causal={causal}", t, 1.0 / math.sqrt(d), causal, dev,
+                           heads=[(0, 0), (0, 1)])
+    assert np.all(G.host_f64(res["dk"])[:, :, 128:256] == 0)
+    assert np.all(G.host_f64(res["dv"])[:, :, 128:256] == 0)
 
 
 def test_invariants_on_device_outputs(dev):
