@@ -212,6 +212,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
     }
     const float msub = (m_used == neg_inf()) ? 0.f : m_used;
 
+    // Wave priority per section (two waves of different workgroups share a SIMD): measured best
+    // with section 1 first at d = 128, section 2 first at d = 64.
+    __builtin_amdgcn_s_setprio(D == 128 ? 1 : 0);
     // section 1: S[t+1], and P[t] = exp2(S[t] * scale * log2(e) - m) in fp32 (kept in s_cur for
     // the row sum, so LSE carries fp32 error only) and rounded to bf16 for PV.
     // pk[2 kb + m2] holds keys k0 + 32 kb + 16 m2 + 8h + 0..7: one k-slot group of the PV MFMA.
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
 
     if (has1) mask_tile(s_nxt, tile_start(t + 1));
 
+    __builtin_amdgcn_s_setprio(D == 128 ? 0 : 1);
     // section 2: O^T += V^T P^T over the 64 keys (4 contraction chunks of 16; V^T read
     // transposed), the row sum of P[t] and the running max after S[t+1]
 #pragma unroll

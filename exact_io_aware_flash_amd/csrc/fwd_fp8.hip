@@ -407,6 +407,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     }
     const float msub = (m_used == neg_inf()) ? 0.f : m_used;
 
+    // wave priority per section (two waves of different workgroups share a SIMD): the PV
+    // section first, as measured
+    __builtin_amdgcn_s_setprio(0);
     // section 1: S[t+1] on the matrix cores; P[t] = exp2(S[t] * scale * log2(e) - m) in fp32
     // (kept in s_cur for the row sums) and as E4M3 codes for PV: byte 16 kb + r of the operand
     // is register r of block kb.  Each MFMA is followed by a share of the exponentials.
@@ -444,6 +447,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
 
     if (has1) mask_tile(s_nxt, tile_start(t + 1));
 
+    __builtin_amdgcn_s_setprio(1);
     // section 2: O^T += V^T P^T over the 64 keys, the row sums of P[t], the max after S[t+1].
     // Written out slot by slot like section 1: each PV MFMA is followed by its share of the row
     // sums and of the running max (V operands read one MFMA ahead).
