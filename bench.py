@@ -10,6 +10,8 @@ resident in device memory.  Prints one JSON line.
     python bench.py --linear-sweep [--copy-calibration 256]     (under rocprofv3 --pmc)
     python bench.py --sweep-from FETCH_CSV WRITE_CSV
     python bench.py --mfma-from COUNTER_CSV
+    python bench.py --data-sensitivity [--workload long]       (alone, or under rocprofv3 --pmc)
+    python bench.py --data-sensitivity-from COUNTER_CSV
 
 HBM traffic: run the bench twice under `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` with
 `--copy-calibration 256`, which first copies 256 MiB with the runtime's copy kernel.  The two
@@ -222,6 +224,115 @@ def mfma_from(csv_path: str) -> str:
     return "\n".join(lines)
 
 
+GEMM_N = 8192                       # the library GEMM timed beside the attention kernels
+SENS_CALLS = 7                      # calls per case in --data-sensitivity (2 warm-up + 5 timed)
+
+
+def timed_calls(fn, warm: int = 2, n: int = 5) -> float:
+    """Median milliseconds of n event-timed calls of fn after warm untimed ones (torch's stream)."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sorted(ts)[len(ts) // 2]
+
+
+def library_gemm(dev, n: int = GEMM_N, fill: str = "randn", warm: int = 2, calls: int = 5):
+    """Rate of the vendor library's bf16 GEMM (torch.matmul, n x n x n) on the same kind of
+    inputs: a reference for what the matrix cores sustain on this part under this data, not a
+    step of the attention path."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(n)
+    if fill == "randn":
+        a, b = (torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16) for _ in range(2))
+    else:
+        a, b = (torch.zeros(n, n, device=dev, dtype=torch.bfloat16) for _ in range(2))
+    ms = timed_calls(lambda: torch.matmul(a, b), warm, calls)
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": f"{n}x{n}x{n} bf16 {'N(0,1)' if fill == 'randn' else 'zeros'}", "ms": ms, "TFLOP/s": tf,
+            "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+
+
+def data_sensitivity(dev, w, q, k, v):
+    """Causal forward at the workload's shape on its N(0,1) inputs, on those inputs times 0.01, on
+    zeros and on ones; then the library GEMM on N(0,1) and on zeros.  Same kernels, same work:
+    any difference is the part's power limit reacting to the data.  SENS_CALLS calls per case,
+    in that order (the counter parser relies on it)."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ff = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    cases = [("N(0,1) (the workload's inputs)", (q, k, v)),
+             ("N(0,1) x 0.01", tuple((x.float() * 0.01).to(torch.bfloat16) for x in (q, k, v))),
+             ("zeros", tuple(torch.zeros_like(q) for _ in range(3))),
+             ("ones", tuple(torch.ones_like(q) for _ in range(3)))]
+    lines = ["| kernel | inputs | ms (median of 5) | TFLOP/s | % of bf16 peak |", "|---|---|---|---|---|"]
+    for name, (a, b, c) in cases:
+        ms = timed_calls(lambda: fa.fwd(a, b, c, w.scale, w.causal, None, out=o, lse=lse), 2, SENS_CALLS - 2)
+        tf = ff / (ms * 1e-3) / 1e12
+        lines.append(f"| attention forward ({w.name}) | {name} | {ms:.3f} | {tf:.0f} | {100 * tf / PEAK_BF16_TFLOPS:.1f} |")
+        print(lines[-1], file=sys.stderr, flush=True)
+    for n in (GEMM_N, 2 * GEMM_N):
+        for fill in ("randn", "zeros"):
+            r = library_gemm(dev, n, fill, 2, SENS_CALLS - 2)
+            lines.append(f"| torch.matmul (vendor library) | {r['shape']} | {r['ms']:.3f} | {r['TFLOP/s']:.0f} | "
+                         f"{100 * r['frac_of_peak']:.1f} |")
+            print(lines[-1], file=sys.stderr, flush=True)
+    return "\n".join(lines)
+
+
+def data_sensitivity_from(csv_path: str) -> str:
+    """Clock and MFMA busy fraction per case of a --data-sensitivity counter run (counters as in
+    --mfma-from).  Dispatches of the forward come in blocks of SENS_CALLS per input case, and so do
+    those of the GEMM kernel (the most frequent other kernel with MFMA instructions)."""
+    import csv
+    import statistics
+
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        dsp = int(r["Dispatch_Id"])
+        e = per.setdefault(dsp, {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    order = [per[d] for d in sorted(per)]
+    fwd = [e for e in order if kernel_label(e["name"]) == "fwd"]
+    others = {}
+    for e in order:
+        if kernel_label(e["name"]) is None and e.get("SQ_INSTS_MFMA", 0.0) > 0:
+            others.setdefault(e["name"], []).append(e)
+    gemm = max(others.values(), key=len) if others else []
+    f_cases = ["N(0,1)", "N(0,1) x 0.01", "zeros", "ones"]
+    g_cases = [f"{GEMM_N}^3 N(0,1)", f"{GEMM_N}^3 zeros", f"{2 * GEMM_N}^3 N(0,1)", f"{2 * GEMM_N}^3 zeros"]
+    lines = ["| kernel | inputs | dispatches | MFMA busy ÷ (1024 SIMDs × kernel cycles) | kernel clock (GHz) |",
+             "|---|---|---|---|---|"]
+    for label, seq, names in (("attention forward", fwd, f_cases), ("library GEMM", gemm, g_cases)):
+        for i, case in enumerate(names):
+            blk = seq[i * SENS_CALLS:(i + 1) * SENS_CALLS][2:]  # the timed calls
+            if not blk:
+                continue
+            util, clk = [], []
+            for e in blk:
+                cycles = e["GRBM_GUI_ACTIVE"] / 8.0
+                util.append(e["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * cycles) if cycles else 0.0)
+                clk.append(cycles / (e["ns"] * 1e-9) / 1e9)
+            lines.append(f"| {label} | {case} | {len(blk)} | {100 * statistics.median(util):.1f}% | "
+                         f"{statistics.median(clk):.2f} |")
+    return "\n".join(lines)
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the current
     kernel sources; else None."""
@@ -356,6 +467,11 @@ def main():
                     help="print HBM bytes per forward call against N from a --linear-sweep counter run and exit")
     ap.add_argument("--mfma-from", metavar="CSV",
                     help="print MFMA utilisation per kernel from an SQ counter run and exit")
+    ap.add_argument("--data-sensitivity", action="store_true",
+                    help="time the forward and the library GEMM on N(0,1), scaled, zero and one inputs and exit")
+    ap.add_argument("--data-sensitivity-from", metavar="CSV",
+                    help="print clock and MFMA busy per case from a --data-sensitivity counter run and exit")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the library GEMM reference figure")
     args = ap.parse_args()
     if args.traffic_from:
         print(traffic_from(*args.traffic_from, workload=args.workload, copy_mib=args.copy_calibration or 256))
@@ -365,6 +481,9 @@ def main():
         return
     if args.mfma_from:
         print(mfma_from(args.mfma_from))
+        return
+    if args.data_sensitivity_from:
+        print(data_sensitivity_from(args.data_sensitivity_from))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -398,6 +517,9 @@ def main():
     do = to_dev(t.do) if not w.fwd_only else None
     mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f}s: {w.description}", file=sys.stderr, flush=True)
+    if args.data_sensitivity:
+        print(data_sensitivity(dev, w, q, k, v), flush=True)
+        return
     B, H, N, d = w.B, w.H, w.N, w.d
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
@@ -500,6 +622,10 @@ def main():
         ms_nc = e[0].elapsed_time(e[1]) / max(3, args.steps // 2)
         tf_nc = fnc / (ms_nc * 1e-3) / 1e12
         line["fwd_noncausal"] = {"ms": ms_nc, "TFLOP/s": tf_nc, "frac_of_peak": tf_nc / PEAK_BF16_TFLOPS}
+    if not args.no_gemm:
+        # the vendor library's bf16 GEMM on N(0,1) inputs in the same process: what the matrix
+        # cores sustain on this part under Gaussian data (context for the fractions above)
+        line["library_gemm"] = library_gemm(dev)
     if not args.no_fp8:
         line["mxfp8_forward"] = fp8_forward(fa, w, q, k, v, mask, ff, max(3, args.steps))
         if not args.no_cpu_baseline:

@@ -84,3 +84,35 @@ def test_mfma_from_busy_fraction(bench, tmp_path):
     table = bench.mfma_from(str(tmp_path / "m.csv"))
     line = [l for l in table.splitlines() if l.startswith("| bwd_dkdv")][0]
     assert "50.0%" in line and "2.00 GHz" in line
+
+
+def test_data_sensitivity_from_groups_cases_in_call_order(bench, tmp_path):
+    # four forward cases, then four GEMM cases, SENS_CALLS dispatches each; a fill kernel without
+    # MFMA instructions in between is ignored.  The first two calls of each case are warm-up.
+    fwd = "void fa::(anonymous namespace)::fwd_bf16_kernel<128, true, false, false>(fa::FwdArgs, fa::Sched)"
+    gemm = "Cijk_Alik_Bljk_BBS_BH_MT256x256x64"
+    n = bench.SENS_CALLS
+    rows, dsp = [], 0
+
+    def add(name, busy, mfma):
+        nonlocal dsp
+        dsp += 1
+        for cname, val in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", 8000), ("SQ_INSTS_MFMA", mfma)):
+            rows.append({"Dispatch_Id": dsp, "Kernel_Name": name, "Counter_Name": cname, "Counter_Value": val,
+                         "Start_Timestamp": 0, "End_Timestamp": 500})
+
+    for case in range(4):
+        for i in range(n):
+            add(fwd, 1024 * 100 * (case + 1) if i >= 2 else 0, 10)
+    add("void at::native::fill_kernel", 0, 0)
+    for case in range(4):
+        for i in range(n):
+            add(gemm, 1024 * 200 * (case + 1) if i >= 2 else 0, 10)
+    _write_counter_csv(tmp_path / "s.csv", rows)
+    table = bench.data_sensitivity_from(str(tmp_path / "s.csv")).splitlines()
+    fwd_lines = [l for l in table if l.startswith("| attention forward")]
+    gemm_lines = [l for l in table if l.startswith("| library GEMM")]
+    assert len(fwd_lines) == 4 and len(gemm_lines) == 4
+    assert "| zeros |" in fwd_lines[2] and "30.0%" in fwd_lines[2] and "2.00" in fwd_lines[2]
+    assert "zeros" in gemm_lines[1] and "40.0%" in gemm_lines[1]
+    assert all(f"| {n - 2} |" in l for l in fwd_lines + gemm_lines)
