@@ -333,6 +333,57 @@ def data_sensitivity_from(csv_path: str) -> str:
     return "\n".join(lines)
 
 
+OTHER_WORKLOADS = ("bert", "gpt2", "sparse")
+
+
+def percentiles(ms_list):
+    """p10 / p50 / p90 of a list of per-call milliseconds (nearest rank)."""
+    v = sorted(ms_list)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"p10_ms": pick(0.1), "p50_ms": pick(0.5), "p90_ms": pick(0.9)}
+
+
+def time_workload(fa, w, dev, steps: int, warmup: int):
+    """Forward and the three backward kernels of one workload on its seeded inputs, each bracketed
+    by events on torch's current stream (the stream the library launches on); medians over
+    `steps` steps, TFLOP/s under the same convention as the main figure."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    t = workloads.make(w, with_do=True)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, do = (to_dev(x) for x in (t.q, t.k, t.v, t.do))
+    mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = fa.new_workspace(B, H, N, d, dev)
+    calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, mask, out=o, lse=lse),
+             lambda: fa.bwd_preprocess(q, o, do, ws),
+             lambda: fa.bwd_dkdv(q, k, v, do, lse, ws, w.scale, w.causal, mask, dk, dv),
+             lambda: fa.bwd_dq(q, k, v, do, lse, ws, w.scale, w.causal, mask, dq)]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    per = [sorted(e[j].elapsed_time(e[j + 1]) for e in ev)[steps // 2] for j in range(len(calls))]
+    ff = workloads.flops_fwd(B, H, N, d, w.causal, t.block_mask)
+    fwd_ms, bwd_ms = per[0], sum(per[1:])
+    return {"config": w.description, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+            "fwd_TFLOP/s": ff / (fwd_ms * 1e-3) / 1e12, "bwd_TFLOP/s": 2.5 * ff / (bwd_ms * 1e-3) / 1e12,
+            "fwd+bwd_TFLOP/s": 3.5 * ff / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the current
     kernel sources; else None."""
@@ -472,6 +523,8 @@ def main():
     ap.add_argument("--data-sensitivity-from", metavar="CSV",
                     help="print clock and MFMA busy per case from a --data-sensitivity counter run and exit")
     ap.add_argument("--no-gemm", action="store_true", help="skip the library GEMM reference figure")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the figures of the d = 64 workloads (BERT-, GPT-2-shaped, block-sparse)")
     args = ap.parse_args()
     if args.traffic_from:
         print(traffic_from(*args.traffic_from, workload=args.workload, copy_mib=args.copy_calibration or 256))
@@ -560,6 +613,7 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
+    kern_pct = {n: percentiles([e[j].elapsed_time(e[j + 1]) for e in events]) for j, n in enumerate(names)}
     gpu_ms = sum(kern_ms.values())
 
     ff = workloads.flops_fwd(B, H, N, d, w.causal, t.block_mask)
@@ -574,6 +628,7 @@ def main():
         else:
             tf = kf[n] / (ms * 1e-3) / 1e12
             kernels[n] = {"ms": ms, "TFLOP/s": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+        kernels[n].update(kern_pct[n])
     dom = max(names, key=lambda n: kern_ms[n])
     if dom == "bwd_preprocess":
         ach = preprocess_bytes(w) / (kern_ms[dom] * 1e-3) / 1e9
@@ -622,6 +677,10 @@ def main():
         ms_nc = e[0].elapsed_time(e[1]) / max(3, args.steps // 2)
         tf_nc = fnc / (ms_nc * 1e-3) / 1e12
         line["fwd_noncausal"] = {"ms": ms_nc, "TFLOP/s": tf_nc, "frac_of_peak": tf_nc / PEAK_BF16_TFLOPS}
+    if args.workload == "long" and not args.no_other_workloads:
+        # the other bf16 workloads (d = 64), each timed kernel by kernel the same way
+        line["other_workloads"] = {n: time_workload(fa, workloads.WORKLOADS[n], dev, max(5, args.steps // 2), 2)
+                                   for n in OTHER_WORKLOADS}
     if not args.no_gemm:
         # the vendor library's bf16 GEMM on N(0,1) inputs in the same process: what the matrix
         # cores sustain on this part under Gaussian data (context for the fractions above)

@@ -116,3 +116,9 @@ def test_data_sensitivity_from_groups_cases_in_call_order(bench, tmp_path):
     assert "| zeros |" in fwd_lines[2] and "30.0%" in fwd_lines[2] and "2.00" in fwd_lines[2]
     assert "zeros" in gemm_lines[1] and "40.0%" in gemm_lines[1]
     assert all(f"| {n - 2} |" in l for l in fwd_lines + gemm_lines)
+
+
+def test_percentiles_nearest_rank(bench):
+    p = bench.percentiles([5.0, 1.0, 4.0, 2.0, 3.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
+    assert p == {"p10_ms": 2.0, "p50_ms": 6.0, "p90_ms": 10.0}
+    assert bench.percentiles([3.0]) == {"p10_ms": 3.0, "p50_ms": 3.0, "p90_ms": 3.0}
