@@ -177,14 +177,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
   wait_dma();
   __syncthreads();
 
-  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..), with the element
-  // masks for the key tail and the causal diagonal.  S = Q K^T and dP = dO V^T of query part s:
+  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..), with the masks for
+  // the key tail and the causal diagonal.  S = Q K^T and dP = dO V^T of query part s:
   // register r of half h holds query 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated in
   // VGPRs by inline-asm MFMAs (the compiler's MFMAs may keep their accumulators in AGPRs, where
   // each VALU read would cost a copy), operand reads two MFMA pairs ahead of their use.  The asm
   // is opaque to the compiler's hazard tracking: a VALU read of S or dP needs 14 wait states
   // after the MFMA that wrote it (gfx950), given after the chain.
-  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc)
+  // `mask`: S starts at -inf where the pair (query, key) is masked (the key tail, and the causal
+  // diagonal for query part qs), instead of 0, so that P = exp(S - LSE) is 0 there with no VALU
+  // work on the scores; the MFMA reading that VALU-written accumulator needs 2 wait states.
+  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, bool mask, int qs)
       __attribute__((always_inline)) {
     bf16x8 qa[DC], oa[DC];
     auto rd = [&](int c) {
@@ -198,7 +201,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
       if (c + 2 < DC) rd(c + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (c == 0) {
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
+        if (mask) {
+          // element r is query qs + 8h + 16 (r / 8) + r % 8: masked when 16 (r / 8) + r % 8 < thr
+          const int thr = key >= N ? 32 : (CAUSAL ? key - qs - 8 * h : 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = 16 * (r >> 3) + (r & 7) < thr ? neg_inf() : 0.f;
+          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(qa[0]), "v"(kreg[0]));
+        }
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pacc) : "v"(oa[0]), "v"(vreg[0]));
       } else {
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
@@ -210,7 +221,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
 
   auto half = [&](const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
     f32x16 sacc, pacc;
-    sp_chain(tq, to, s, sacc, pacc);
+    // parts that reach the key tail or the causal diagonal of this wave's keys
+    const bool mask = (k0w + 32 > N) || (CAUSAL && qs < k0w + 31);
+    sp_chain(tq, to, s, sacc, pacc, mask, qs);
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
     // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
     bf16x8 pp[2], dsp[2];
@@ -225,9 +238,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
         const int r = 8 * mm + e;
         const float lv = e < 4 ? l0[e] : l1[e - 4];
         const float dv = e < 4 ? d0[e] : d1[e - 4];
-        float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
-        const int qi = qs + 16 * mm + 8 * h + e;
-        if (key >= N || (CAUSAL && key > qi)) p = 0.f;
+        const float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
         pp[mm][e] = (__bf16)p;
         dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
       }
@@ -268,8 +279,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
     }
     const float* Ls = lbuf[par];
     const float* Ds = dbuf[par];
-    // one body (with the element masks) for every tile: a second copy would cost the kernel its
-    // second workgroup per CU; queries past N need no mask (their LSE is +inf, so P = 0)
+    // queries past N need no mask (their LSE is +inf, so P = 0)
 #pragma unroll
     for (int s = 0; s < NH; ++s) {
       const int qs = q0 + 32 * s;
