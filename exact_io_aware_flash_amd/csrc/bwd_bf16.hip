@@ -177,18 +177,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
   wait_dma();
   __syncthreads();
 
-  // One 32-query half (rows 32 s .. 32 s + 31 of the tile, queries qs ..), with the masks for
-  // the key tail and the causal diagonal.  S = Q K^T and dP = dO V^T of query part s:
-  // register r of half h holds query 32 s + acc_row(r, h) of the tile, key `key`.  Accumulated in
-  // VGPRs by inline-asm MFMAs (the compiler's MFMAs may keep their accumulators in AGPRs, where
-  // each VALU read would cost a copy), operand reads two MFMA pairs ahead of their use.  The asm
-  // is opaque to the compiler's hazard tracking: a VALU read of S or dP needs 14 wait states
-  // after the MFMA that wrote it (gfx950), given after the chain.
-  // `mask`: S starts at -inf where the pair (query, key) is masked (the key tail, and the causal
-  // diagonal for query part qs), instead of 0, so that P = exp(S - LSE) is 0 there with no VALU
-  // work on the scores; the MFMA reading that VALU-written accumulator needs 2 wait states.
-  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, bool mask, int qs)
-      __attribute__((always_inline)) {
+  // S = Q K^T and dP = dO V^T of 32-query part s (rows 32 s .. 32 s + 31 of the tile, queries
+  // qs ..): register r of half h holds query 32 s + acc_row(r, h) of the tile, key `key`.
+  // Accumulated in VGPRs by inline-asm MFMAs (the compiler's MFMAs may keep their accumulators in
+  // AGPRs, where each VALU read would cost a copy), operand reads two MFMA pairs ahead of their
+  // use; `hook(c)` runs after MFMA pair c in the same fenced slot (independent VALU work, issued
+  // while the MFMAs run).  `mask`: S starts at -inf where the pair (query, key) is masked (the key
+  // tail, and the causal diagonal for query part qs), instead of 0, so that P = exp(S - LSE) is 0
+  // there with no VALU work on the scores; the MFMA reading that VALU-written accumulator needs 2
+  // wait states.  The asm is opaque to the compiler's hazard tracking: a VALU read of S or dP
+  // needs 14 wait states after the MFMA that wrote it (gfx950), given after the chain.
+  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, bool mask, int qs,
+                      auto hook) __attribute__((always_inline)) {
     bf16x8 qa[DC], oa[DC];
     auto rd = [&](int c) {
       qa[c] = lds_b128(tq + raddr[c] + 32 * s * D * 2);
@@ -215,37 +215,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(qa[c]), "v"(kreg[c]));
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pacc) : "v"(oa[c]), "v"(vreg[c]));
       }
+      hook(c);
       __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
   };
 
-  auto half = [&](const char* tq, const char* to, const float* Ls, const float* Ds, int s, int qs) {
-    f32x16 sacc, pacc;
-    // parts that reach the key tail or the causal diagonal of this wave's keys
-    const bool mask = (k0w + 32 > N) || (CAUSAL && qs < k0w + 31);
-    sp_chain(tq, to, s, sacc, pacc, mask, qs);
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
-    // P = exp(S - LSE) and dS = P (dP - D) as bf16 A operands: pp/dsp[mm] = queries 16mm+8h+0..7
-    bf16x8 pp[2], dsp[2];
+  // P = exp(S - LSE) and dS = P (dP - D) of elements 4 qq .. 4 qq + 3 of part s (queries
+  // 16 (qq / 2) + 8h + 4 (qq % 2) + 0..3) as bf16 A operands: pp / dsp[mm] hold queries
+  // 16 mm + 8h + 0..7.  Rows past N, and rows that see no key, have LSE = +inf here, so P = 0.
+  auto pds_quarter = [&](const f32x16& x, const f32x16& y, const f32x4& l, const f32x4& d, int qq,
+                         bf16x8(&pp)[2], bf16x8(&dsp)[2]) __attribute__((always_inline)) {
+    const int mm = qq >> 1, e0 = 4 * (qq & 1);
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(Ls + 32 * s + 16 * mm + 8 * h);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(Ls + 32 * s + 16 * mm + 8 * h + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + 32 * s + 16 * mm + 8 * h);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + 32 * s + 16 * mm + 8 * h + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * mm + e;
-        const float lv = e < 4 ? l0[e] : l1[e - 4];
-        const float dv = e < 4 ? d0[e] : d1[e - 4];
-        const float p = fast_exp2(__builtin_fmaf(sacc[r], sl, -lv));
-        pp[mm][e] = (__bf16)p;
-        dsp[mm][e] = (__bf16)(p * (pacc[r] - dv));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * mm + e0 + e;
+      const float p = fast_exp2(__builtin_fmaf(x[r], sl, -l[e]));
+      pp[mm][e0 + e] = (__bf16)p;
+      dsp[mm][e0 + e] = (__bf16)(p * (y[r] - d[e]));
     }
-    // dV += P^T dO ; dK += dS^T Q (contraction over the 32 queries, two chunks of 16); each MFMA
-    // takes one transposed B operand (two 8-byte transposing reads), kept four MFMAs ahead (one
-    // wave per SIMD: nothing else hides the read latency)
+  };
+  auto stat4 = [&](const float* rows, int s, int qq) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(rows + 32 * s + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1));
+  };
+
+  // dV += P^T dO ; dK += dS^T Q for part s (contraction over its 32 queries, two chunks of 16);
+  // each MFMA takes one transposed B operand (two 8-byte transposing reads), kept four MFMAs ahead
+  auto dvdk = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const bf16x8(&dsp)[2])
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -263,8 +261,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // One query tile, its four 32-query parts software-pipelined within the wave: the S / dP MFMAs
+  // of part s + 1 carry P and dS of part s in their slots (one quarter of the part's elements per
+  // MFMA pair, its row statistics read one slot ahead), then the dV / dK MFMAs of part s run.
+  // Every part is computed, also one that lies wholly above the causal diagonal or past N: its
+  // masks (or its LSE of +inf) make P and dS zero, so it adds nothing.
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tq = par ? qbuf1 : qbuf0;
@@ -279,13 +283,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
     }
     const float* Ls = lbuf[par];
     const float* Ds = dbuf[par];
-    // queries past N need no mask (their LSE is +inf, so P = 0)
+    // parts that reach the key tail or the causal diagonal of this wave's keys
+    auto part_mask = [&](int qs) -> bool { return (k0w + 32 > N) || (CAUSAL && qs < k0w + 31); };
+    f32x16 sv[2], pv[2];  // S and dP of part s in sv / pv[s & 1]
+    sp_chain(tq, to, 0, sv[0], pv[0], part_mask(q0), q0, [](int) {});
 #pragma unroll
     for (int s = 0; s < NH; ++s) {
-      const int qs = q0 + 32 * s;
-      if (qs >= N) continue;
-      if (CAUSAL && qs + 31 < k0w) continue;  // every query of this half precedes every key of the wave
-      half(tq, to, Ls, Ds, s, qs);
+      bf16x8 pp[2], dsp[2];
+      const f32x16& x = sv[s & 1];
+      const f32x16& y = pv[s & 1];
+      f32x4 l = stat4(Ls, s, 0), d = stat4(Ds, s, 0);
+      auto quarter = [&](int qq) __attribute__((always_inline)) {
+        const f32x4 lc = l, dc = d;
+        if (qq + 1 < 4) {
+          l = stat4(Ls, s, qq + 1);
+          d = stat4(Ds, s, qq + 1);
+        }
+        pds_quarter(x, y, lc, dc, qq, pp, dsp);
+        if (qq & 1) {
+          asm volatile("" : "+v"(pp[qq >> 1]), "+v"(dsp[qq >> 1]));  // computed in this slot
+        }
+      };
+      if (s + 1 < NH) {
+        const int qs1 = q0 + 32 * (s + 1);
+        sp_chain(tq, to, s + 1, sv[(s + 1) & 1], pv[(s + 1) & 1], part_mask(qs1), qs1, quarter);
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) quarter(qq);
+      }
+      dvdk(tq, to, s, pp, dsp);
     }
     if (has_next) rowstats_store(par ^ 1);
     wait_dma();
