@@ -88,6 +88,15 @@ def kernel_label(name: str):
     return None
 
 
+def check_one_kernel_per_label(names_by_label: dict, path: str):
+    """A label must stand for one kernel instantiation: a counter run that also launched the
+    kernels of other shapes (the d = 64 workloads of the default bench line) would mix them."""
+    mixed = {k: sorted(v) for k, v in names_by_label.items() if len(v) > 1}
+    if mixed:
+        raise SystemExit(f"{path}: several kernels under one label {sorted(mixed)}; profile the bench with "
+                         "--no-other-workloads --no-gemm")
+
+
 def read_counter(path: str, counter: str):
     """{dispatch id: (kernel name, counter value summed over the rows of that dispatch)}."""
     import csv
@@ -119,10 +128,13 @@ def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_mib: int = 
             raise SystemExit(f"{path}: no {COPY_KERNEL} dispatch; run the bench with --copy-calibration {copy_mib}")
         factor = copy_bytes / (statistics.median(copies) * 1024.0)
         out[counter.lower() + "_factor"] = factor
+        names = {}
         for name, v in vals.values():
             short = kernel_label(name)
             if short:
+                names.setdefault(short, set()).add(name)
                 per_kernel.setdefault(short, {}).setdefault(counter, []).append(v * 1024.0 * factor)
+        check_one_kernel_per_label(names, path)
     lines = [f"| kernel | dispatches | FETCH bytes/launch | WRITE bytes/launch | HBM bytes/launch |",
              "|---|---|---|---|---|"]
     for short, c in per_kernel.items():
@@ -208,6 +220,8 @@ def mfma_from(csv_path: str) -> str:
         e = per.setdefault(dsp, {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     out = {}
+    check_one_kernel_per_label({lab: {e["name"] for e in per.values() if kernel_label(e["name"]) == lab}
+                                for lab in {kernel_label(e["name"]) for e in per.values()} if lab}, csv_path)
     for e in per.values():
         short = kernel_label(e["name"])
         if short and "SQ_VALU_MFMA_BUSY_CYCLES" in e:

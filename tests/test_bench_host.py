@@ -122,3 +122,16 @@ def test_percentiles_nearest_rank(bench):
     p = bench.percentiles([5.0, 1.0, 4.0, 2.0, 3.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
     assert p == {"p10_ms": 2.0, "p50_ms": 6.0, "p90_ms": 10.0}
     assert bench.percentiles([3.0]) == {"p10_ms": 3.0, "p50_ms": 3.0, "p90_ms": 3.0}
+
+
+def test_counter_summaries_refuse_mixed_kernels(bench, tmp_path):
+    # the d = 64 forward of another workload under the same label as the d = 128 one: refused
+    rows = []
+    for dsp, name in ((1, "void fa::(anonymous namespace)::fwd_bf16_kernel<128, true, false, false>(fa::FwdArgs, fa::Sched)"),
+                      (2, "void fa::(anonymous namespace)::fwd_bf16_kernel<64, true, false, false>(fa::FwdArgs, fa::Sched)")):
+        for cname, val in (("SQ_VALU_MFMA_BUSY_CYCLES", 1000), ("GRBM_GUI_ACTIVE", 8000), ("SQ_INSTS_MFMA", 10)):
+            rows.append({"Dispatch_Id": dsp, "Kernel_Name": name, "Counter_Name": cname, "Counter_Value": val,
+                         "Start_Timestamp": 0, "End_Timestamp": 500})
+    _write_counter_csv(tmp_path / "m.csv", rows)
+    with pytest.raises(SystemExit, match="no-other-workloads"):
+        bench.mfma_from(str(tmp_path / "m.csv"))
