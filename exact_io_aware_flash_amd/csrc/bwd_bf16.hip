@@ -221,54 +221,74 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc), "+v"(pacc));  // 16 wait states
   };
 
-  // P = exp(S - LSE) and dS = P (dP - D) of elements 4 qq .. 4 qq + 3 of part s (queries
-  // 16 (qq / 2) + 8h + 4 (qq % 2) + 0..3) as bf16 A operands: pp / dsp[mm] hold queries
-  // 16 mm + 8h + 0..7.  Rows past N, and rows that see no key, have LSE = +inf here, so P = 0.
-  auto pds_quarter = [&](const f32x16& x, const f32x16& y, const f32x4& l, const f32x4& d, int qq,
-                         bf16x8(&pp)[2], bf16x8(&dsp)[2]) __attribute__((always_inline)) {
+  // Score elements 4 qq .. 4 qq + 3 of a part are queries 16 (qq / 2) + 8h + 4 (qq % 2) + 0..3;
+  // pp / dsp[mm] (bf16 A operands) hold queries 16 mm + 8h + 0..7.  Rows past N, and rows that
+  // see no key, have LSE = +inf here, so P = 0 there.
+  auto stat4 = [&](const float* rows, int s, int qq) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(rows + 32 * s + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1));
+  };
+  // P = exp(S - LSE) of quarter qq, written over S in place (fp32, for dS) and as bf16 into pp
+  auto p_quarter = [&](f32x16& x, const f32x4& l, int qq, bf16x8(&pp)[2]) __attribute__((always_inline)) {
     const int mm = qq >> 1, e0 = 4 * (qq & 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 8 * mm + e0 + e;
       const float p = fast_exp2(__builtin_fmaf(x[r], sl, -l[e]));
+      x[r] = p;
       pp[mm][e0 + e] = (__bf16)p;
-      dsp[mm][e0 + e] = (__bf16)(p * (y[r] - d[e]));
     }
   };
-  auto stat4 = [&](const float* rows, int s, int qq) -> f32x4 {
-    return *reinterpret_cast<const f32x4*>(rows + 32 * s + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1));
+  // dS = P (dP - D) of quarter qq, from P (in x) and dP (in y)
+  auto ds_quarter = [&](const f32x16& x, const f32x16& y, const f32x4& d, int qq, bf16x8(&dsp)[2])
+      __attribute__((always_inline)) {
+    const int mm = qq >> 1, e0 = 4 * (qq & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * mm + e0 + e;
+      dsp[mm][e0 + e] = (__bf16)(x[r] * (y[r] - d[e]));
+    }
   };
 
-  // dV += P^T dO ; dK += dS^T Q for part s (contraction over its 32 queries, two chunks of 16);
-  // each MFMA takes one transposed B operand (two 8-byte transposing reads), kept four MFMAs ahead
-  auto dvdk = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const bf16x8(&dsp)[2])
-      __attribute__((always_inline)) {
+  // dV += P^T dO, then dK += dS^T Q, for part s (contraction over its 32 queries, two chunks of
+  // 16; MFMA i takes feature block i / 2 and chunk i % 2).  Each MFMA takes one transposed B
+  // operand (two 8-byte transposing reads), read two MFMAs ahead.  dS of quarter i is computed in
+  // the slot of dV MFMA i (D read one slot ahead), so the dK MFMAs find it complete.
+  auto dvdk = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const f32x16& x, const f32x16& y,
+                  const float* Ds) __attribute__((always_inline)) {
+    static_assert(DB == 2, "four MFMAs per product at d = 64");
+    bf16x8 ob[4], qb[4], dsp[2];
+    auto trd = [&](const char* t, int i) -> bf16x8 {
+      const int db = i >> 1, roff = (32 * s + 16 * (i & 1)) * D * 2;
+      return join8(lds_tr4(t + roff + taddr[0][db]), lds_tr4(t + roff + taddr[1][db]));
+    };
+    ob[0] = trd(to, 0);
+    ob[1] = trd(to, 1);
+    f32x4 d = stat4(Ds, s, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int roff = (32 * s + 16 * mm) * D * 2;
-        dvacc[db] = mfma32(pp[mm], join8(lds_tr4(to + roff + taddr[0][db]), lds_tr4(to + roff + taddr[1][db])),
-                           dvacc[db]);
-        dkacc[db] = mfma32(dsp[mm], join8(lds_tr4(tq + roff + taddr[0][db]), lds_tr4(tq + roff + taddr[1][db])),
-                           dkacc[db]);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-    for (int i = 0; i < 4 * DB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    for (int i = 0; i < 4; ++i) {
+      if (i + 2 < 4) ob[i + 2] = trd(to, i + 2);
+      else qb[i - 2] = trd(tq, i - 2);
+      const f32x4 dc = d;
+      if (i + 1 < 4) d = stat4(Ds, s, i + 1);
+      dvacc[i >> 1] = mfma32(pp[i & 1], ob[i], dvacc[i >> 1]);
+      ds_quarter(x, y, dc, i, dsp);
+      if (i & 1) asm volatile("" : "+v"(dsp[i >> 1]));  // computed in this slot
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 2 < 4) qb[i + 2] = trd(tq, i + 2);
+      dkacc[i >> 1] = mfma32(dsp[i & 1], qb[i], dkacc[i >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // One query tile, its four 32-query parts software-pipelined within the wave: the S / dP MFMAs
-  // of part s + 1 carry P and dS of part s in their slots (one quarter of the part's elements per
-  // MFMA pair, its row statistics read one slot ahead), then the dV / dK MFMAs of part s run.
-  // Every part is computed, also one that lies wholly above the causal diagonal or past N: its
-  // masks (or its LSE of +inf) make P and dS zero, so it adds nothing.
+  // of part s + 1 carry P of part s in their slots (a quarter of the part's elements per MFMA
+  // pair, the LSE read one slot ahead), then the dV MFMAs of part s carry its dS, then its dK
+  // MFMAs run.  Every part is computed, also one that lies wholly above the causal diagonal or
+  // past N: its masks (or its LSE of +inf) make P and dS zero, so it adds nothing.
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;
     const char* tq = par ? qbuf1 : qbuf0;
@@ -285,24 +305,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
     const float* Ds = dbuf[par];
     // parts that reach the key tail or the causal diagonal of this wave's keys
     auto part_mask = [&](int qs) -> bool { return (k0w + 32 > N) || (CAUSAL && qs < k0w + 31); };
-    f32x16 sv[2], pv[2];  // S and dP of part s in sv / pv[s & 1]
+    f32x16 sv[2], pv[2];  // S (then P) and dP of part s in sv / pv[s & 1]
     sp_chain(tq, to, 0, sv[0], pv[0], part_mask(q0), q0, [](int) {});
 #pragma unroll
     for (int s = 0; s < NH; ++s) {
-      bf16x8 pp[2], dsp[2];
-      const f32x16& x = sv[s & 1];
-      const f32x16& y = pv[s & 1];
-      f32x4 l = stat4(Ls, s, 0), d = stat4(Ds, s, 0);
+      bf16x8 pp[2];
+      f32x16& x = sv[s & 1];
+      f32x4 l = stat4(Ls, s, 0);
       auto quarter = [&](int qq) __attribute__((always_inline)) {
-        const f32x4 lc = l, dc = d;
-        if (qq + 1 < 4) {
-          l = stat4(Ls, s, qq + 1);
-          d = stat4(Ds, s, qq + 1);
-        }
-        pds_quarter(x, y, lc, dc, qq, pp, dsp);
-        if (qq & 1) {
-          asm volatile("" : "+v"(pp[qq >> 1]), "+v"(dsp[qq >> 1]));  // computed in this slot
-        }
+        const f32x4 lc = l;
+        if (qq + 1 < 4) l = stat4(Ls, s, qq + 1);
+        p_quarter(x, lc, qq, pp);
+        if (qq & 1) asm volatile("" : "+v"(pp[qq >> 1]));  // computed in this slot
       };
       if (s + 1 < NH) {
         const int qs1 = q0 + 32 * (s + 1);
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) quarter(qq);
       }
-      dvdk(tq, to, s, pp, dsp);
+      dvdk(tq, to, s, pp, x, pv[s & 1], Ds);
     }
     if (has_next) rowstats_store(par ^ 1);
     wait_dma();
