@@ -38,7 +38,7 @@ namespace {
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
   constexpr int BR = 128, BC = 64;
   constexpr int DC = D / 16;  // 16-wide contraction chunks over d
   constexpr int DB = D / 32;  // 32-row output blocks over d
