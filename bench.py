@@ -72,7 +72,7 @@ def preprocess_bytes(w):
 
 
 KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_delta_kernel": "bwd_preprocess",
-               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "fwd_mxfp8_kernel": "fwd_mxfp8",
+               "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dkdv_wave_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "fwd_mxfp8_kernel": "fwd_mxfp8",
                "mx_quantize_rows_kernel": "mxfp8_quantize_rows", "mx_quantize_vt_kernel": "mxfp8_quantize_vt"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 

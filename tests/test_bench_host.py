@@ -31,6 +31,8 @@ def test_kernel_labels(bench):
     assert lab("void fa::(anonymous namespace)::fwd_bf16_kernel<64, false, true, false>(fa::FwdArgs, fa::Sched)") == \
         "fwd_noncausal"
     assert lab("void fa::(anonymous namespace)::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs, fa::Sched)") == "bwd_dkdv"
+    assert lab("void fa::(anonymous namespace)::bwd_dkdv_wave_kernel<64, true, false>(fa::BwdArgs, fa::Sched)") == \
+        "bwd_dkdv"
     assert lab("void fa::(anonymous namespace)::fwd_mxfp8_kernel<128, true, false>(fa::Fp8FwdArgs, fa::Sched)") == \
         "fwd_mxfp8"
     assert lab("_ZN2fa12_GLOBAL__N_121mx_quantize_vt_kernelILi128EEEvPKDF16bPhS4_ii") == "mxfp8_quantize_vt"
