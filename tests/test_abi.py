@@ -95,6 +95,21 @@ def test_fwd_argument_errors(L, f32):
     assert fwd_call(L, q, k, v, o, ctypes.c_void_p(o.value + 64), f32=f32) == fa.FA_ERR_ALIAS
 
 
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_size_limits(L, f32):
+    """Shapes beyond the documented limits are refused before any HIP call: B*H above 2^30, one
+    head's float32 slice beyond a 31-bit byte range, more than 2^31 - 1 query tiles, and (fp32
+    kernels, which put B*H on grid.y) B*H above 65535.  Every case here fails validation, so the
+    fake pointers are never used."""
+    import exact_io_aware_flash_amd as fa
+    q, k, v, o, lse = ptrs(5)
+    assert fwd_call(L, q, k, v, o, lse, B=1 << 16, H=1 << 15, N=1, f32=f32) == fa.FA_ERR_SHAPE
+    assert fwd_call(L, q, k, v, o, lse, N=1 << 22, d=128, f32=f32) == fa.FA_ERR_SHAPE
+    assert fwd_call(L, q, k, v, o, lse, B=1 << 15, H=1 << 15, N=256, f32=f32) == fa.FA_ERR_SHAPE
+    if f32:
+        assert fwd_call(L, q, k, v, o, lse, B=65536, H=1, N=1, f32=True) == fa.FA_ERR_SHAPE
+
+
 def test_fwd_mask_limit(L):
     import exact_io_aware_flash_amd as fa
     q, k, v, o, lse, m = ptrs(6)
