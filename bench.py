@@ -10,6 +10,7 @@ resident in device memory.  Prints one JSON line.
     python bench.py --linear-sweep [--copy-calibration 256]     (under rocprofv3 --pmc)
     python bench.py --sweep-from FETCH_CSV WRITE_CSV
     python bench.py --mfma-from COUNTER_CSV
+    python bench.py --counters-from COUNTER_CSV
     python bench.py --data-sensitivity [--workload long]       (alone, or under rocprofv3 --pmc)
     python bench.py --data-sensitivity-from COUNTER_CSV
 
@@ -398,6 +399,39 @@ def time_workload(fa, w, dev, steps: int, warmup: int):
             "fwd+bwd_TFLOP/s": 3.5 * ff / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
 
 
+def counters_from(csv_path: str) -> str:
+    """Markdown table of every counter in a rocprofv3 counter file, per attention kernel: the
+    median over its dispatches of each counter summed over the dispatch's rows, and for the SQ
+    wait / active counters their ratio to SQ_WAVE_CYCLES (the share of the waves' cycles)."""
+    import csv
+    import statistics
+
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    check_one_kernel_per_label({lab: {e["name"] for e in per.values() if kernel_label(e["name"]) == lab}
+                                for lab in {kernel_label(e["name"]) for e in per.values()} if lab}, csv_path)
+    names = sorted({k for e in per.values() for k in e if k != "name"})
+    by = {}
+    for e in per.values():
+        lab = kernel_label(e["name"])
+        if lab:
+            by.setdefault(lab, []).append(e)
+    lines = ["| kernel | dispatches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for lab, es in by.items():
+        cells = []
+        for n in names:
+            v = statistics.median(e.get(n, 0.0) for e in es)
+            cell = f"{v:.4g}"
+            wc = statistics.median(e.get("SQ_WAVE_CYCLES", 0.0) for e in es)
+            if wc and (n.startswith("SQ_WAIT") or n.startswith("SQ_ACTIVE_INST")):
+                cell += f" ({100 * v / wc:.1f}%)"
+            cells.append(cell)
+        lines.append(f"| {lab} | {len(es)} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the current
     kernel sources; else None."""
@@ -532,6 +566,8 @@ def main():
                     help="print HBM bytes per forward call against N from a --linear-sweep counter run and exit")
     ap.add_argument("--mfma-from", metavar="CSV",
                     help="print MFMA utilisation per kernel from an SQ counter run and exit")
+    ap.add_argument("--counters-from", metavar="CSV",
+                    help="print every counter of a counter run per kernel (with shares of SQ_WAVE_CYCLES) and exit")
     ap.add_argument("--data-sensitivity", action="store_true",
                     help="time the forward and the library GEMM on N(0,1), scaled, zero and one inputs and exit")
     ap.add_argument("--data-sensitivity-from", metavar="CSV",
@@ -548,6 +584,9 @@ def main():
         return
     if args.mfma_from:
         print(mfma_from(args.mfma_from))
+        return
+    if args.counters_from:
+        print(counters_from(args.counters_from))
         return
     if args.data_sensitivity_from:
         print(data_sensitivity_from(args.data_sensitivity_from))
