@@ -137,3 +137,20 @@ def test_counter_summaries_refuse_mixed_kernels(bench, tmp_path):
     _write_counter_csv(tmp_path / "m.csv", rows)
     with pytest.raises(SystemExit, match="no-other-workloads"):
         bench.mfma_from(str(tmp_path / "m.csv"))
+
+
+def test_counters_from_shares_of_wave_cycles(bench, tmp_path):
+    # two dispatches of the dK/dV kernel: medians of the per-dispatch sums, wait and active
+    # counters also as a share of SQ_WAVE_CYCLES
+    name = "void fa::(anonymous namespace)::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs, fa::Sched)"
+    rows = []
+    for dsp, scale in ((1, 1.0), (2, 1.0)):
+        for cname, val in (("SQ_WAVE_CYCLES", 1000.0), ("SQ_WAIT_ANY", 250.0), ("SQ_LDS_BANK_CONFLICT", 0.0)):
+            for part in range(2):  # rows of one dispatch are summed
+                rows.append({"Dispatch_Id": dsp, "Kernel_Name": name, "Counter_Name": cname,
+                             "Counter_Value": val * scale / 2, "Start_Timestamp": 0, "End_Timestamp": 1})
+    _write_counter_csv(tmp_path / "c.csv", rows)
+    table = bench.counters_from(str(tmp_path / "c.csv")).splitlines()
+    assert table[0].startswith("| kernel | dispatches | SQ_LDS_BANK_CONFLICT | SQ_WAIT_ANY | SQ_WAVE_CYCLES |")
+    line = [l for l in table if l.startswith("| bwd_dkdv")][0]
+    assert "| 2 |" in line and "250 (25.0%)" in line and "| 1000 |" in line
