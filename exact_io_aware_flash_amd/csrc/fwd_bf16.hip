@@ -139,16 +139,25 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(lds_b128(tk + kaddr[c] + 32 * kb * D * 2), qreg[c], s[kb]);
   };
-  // element masks: the causal diagonal and the key tail (only tiles that reach either)
+  // element masks: the causal diagonal and the key tail (only tiles that reach either).  With the
+  // causal mask, register r of half h holds key base + c(r) with base = k0 + 32 kb + 8h and
+  // c(r) = acc_row(r, 0), a constant; the key is masked when it is past N - 1 or past the lane's
+  // query, i.e. when c(r) exceeds one per-lane threshold: one compare and one select per score on
+  // the diagonal tiles.  Without it only the last tile is masked (the key tail).
   auto mask_tile = [&](f32x16(&s)[2], int k0) {
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (CAUSAL) {
+          const int thr = min(qrow, N - 1) - (k0 + 32 * kb + 8 * h);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + acc_row(r, h);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
+          for (int r = 0; r < 16; ++r) s[kb][r] = acc_row(r, 0) > thr ? neg_inf() : s[kb][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + 32 * kb + acc_row(r, h) >= N) s[kb][r] = neg_inf();
         }
+      }
     }
   };
   // online softmax: the running max (scaled log2 units) moves only when a score exceeds it by
