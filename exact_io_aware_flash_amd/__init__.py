@@ -103,6 +103,18 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context for the binding's own allocations.  With an explicit stream, tensors the binding
+    allocates (outputs, the backward workspace, the split-key partials) are allocated on that
+    stream, so the caching allocator does not hand their memory to later work on another stream
+    while the kernels enqueued on `stream` may still use it."""
+    import contextlib
+
+    import torch
+
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _check(t, name, dtype, shape, device):
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -136,10 +148,11 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_mask=No
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(t, name, q.dtype, (B, H, N, d), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     _check(out, "out", q.dtype, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     bm = _mask_arg(block_mask, N, dev)
@@ -169,14 +182,16 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, b
         _check(t, name, q.dtype, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    with _on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check(t, name, q.dtype, (B, H, N, d), dev)
-    need = workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        need = workspace_bytes(B, H, N, d)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     bm = _mask_arg(block_mask, N, dev)
     L = lib()
     if q.dtype == torch.bfloat16:
@@ -221,15 +236,17 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, block
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(t, name, torch.bfloat16, (B, H, N, d), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    with _on(stream):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
     _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
-    if workspace is None:
-        need = splitkv_workspace_bytes(B, H, N, d, splits)
-        if need == 0:
-            raise FlashAttnError(FA_ERR_SPLITS, "fwd_splitkv")
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if workspace is None:
+            need = splitkv_workspace_bytes(B, H, N, d, splits)
+            if need == 0:
+                raise FlashAttnError(FA_ERR_SPLITS, "fwd_splitkv")
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     bm = _mask_arg(block_mask, N, dev)
     st = lib().flash_attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
                                       int(bool(causal)), _ptr(bm), int(splits), _ptr(workspace), _ws_bytes(workspace),
@@ -250,8 +267,9 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
     dev = o_parts.device
     _check(o_parts, "o_parts", torch.float32, (P, *rows_shape, d), dev)
     _check(lse_parts, "lse_parts", torch.float32, (P, *rows_shape), dev)
-    out = torch.empty((*rows_shape, d), dtype=torch.bfloat16, device=dev) if out is None else out
-    lse = torch.empty(rows_shape, dtype=torch.float32, device=dev) if lse is None else lse
+    with _on(stream):
+        out = torch.empty((*rows_shape, d), dtype=torch.bfloat16, device=dev) if out is None else out
+        lse = torch.empty(rows_shape, dtype=torch.float32, device=dev) if lse is None else lse
     _check(out, "out", torch.bfloat16, (*rows_shape, d), dev)
     _check(lse, "lse", torch.float32, rows_shape, dev)
     rows = int(math.prod(rows_shape))
@@ -283,7 +301,8 @@ def bwd_preprocess(q, o, do, workspace=None, stream=None):
     B, H, N, d = o.shape
     for name, t in (("q", q), ("o", o), ("do", do)):
         _check(t, name, torch.bfloat16, (B, H, N, d), o.device)
-    workspace = new_workspace(B, H, N, d, o.device) if workspace is None else workspace
+    with _on(stream):
+        workspace = new_workspace(B, H, N, d, o.device) if workspace is None else workspace
     st = lib().flash_attn_bwd_preprocess(_ptr(q), _ptr(o), _ptr(do), _ptr(workspace), _ws_bytes(workspace), B, H,
                                          N, d, _stream(stream))
     if st != FA_OK:
@@ -300,8 +319,9 @@ def bwd_dkdv(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=N
         _check(t, name, torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    with _on(stream):
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
     bm = _mask_arg(block_mask, N, dev)
     st = lib().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
                                    _ws_bytes(workspace), _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
@@ -320,7 +340,8 @@ def bwd_dq(q, k, v, do, lse, workspace, scale=None, causal=False, block_mask=Non
         _check(t, name, torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
+    with _on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
     bm = _mask_arg(block_mask, N, dev)
     st = lib().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
                                  _ws_bytes(workspace), _ptr(dq), B, H, N, d, scale, int(bool(causal)), _ptr(bm),
@@ -357,13 +378,15 @@ def mxfp8_quantize(x, transposed: bool = False, stream=None) -> MXFP8:
     L = lib()
     if transposed:
         npad = mxfp8_vt_cols(N)
-        codes = torch.empty((B, H, d, npad), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((B, H, npad // 32, 32, d // 32), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            codes = torch.empty((B, H, d, npad), dtype=torch.uint8, device=x.device)
+            scales = torch.empty((B, H, npad // 32, 32, d // 32), dtype=torch.uint8, device=x.device)
         st = L.flash_attn_mxfp8_quantize_vt(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, _stream(stream))
         where = "flash_attn_mxfp8_quantize_vt"
     else:
-        codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+            scales = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=x.device)
         st = L.flash_attn_mxfp8_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, _stream(stream))
         where = "flash_attn_mxfp8_quantize_rows"
     if st != FA_OK:
@@ -389,10 +412,11 @@ def fwd_mxfp8(q: MXFP8, k: MXFP8, vt: MXFP8, scale: float | None = None, causal:
     _check(vt.codes, "vt.codes", torch.uint8, (B, H, d, npad), dev)
     _check(vt.scales, "vt.scales", torch.uint8, (B, H, npad // 32, 32, d // 32), dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
     bm = _mask_arg(block_mask, N, dev)

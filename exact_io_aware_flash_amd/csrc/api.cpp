@@ -24,16 +24,18 @@ int check_common(int B, int H, int N, int d, float scale, int causal, const uint
                  long long* elems) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (!std::isfinite(scale) || scale == 0.f) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  // one head's slice must be a 31-bit byte range (checked first: it bounds N * d to 2^29, so
+  // the products below stay far inside 64 bits)
+  if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_SHAPE;
   const long long bh = (long long)B * H;
   if (bh > (1LL << 30)) return FA_ERR_SHAPE;
-  const long long e = bh * N * d;
+  const long long e = bh * ((long long)N * d);
   if (e <= 0 || e >= kMaxElems / 4) return FA_ERR_SHAPE;
   const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   if (block_mask && bf16 && nb > FA_MAX_MASK_BLOCKS) return FA_ERR_SHAPE;
   if (!bf16 && bh > 65535) return FA_ERR_SHAPE;  // the fp32 kernels put B*H on grid.y
-  if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_SHAPE;  // one head's slice, as a 31-bit byte range
   const long long tiles = bh * ((N + 127) / 128);
   if (tiles > 0x7fffffffLL) return FA_ERR_SHAPE;
   *elems = e;
@@ -63,8 +65,6 @@ size_t workspace_bytes(int B, int H, int N, int d) {
   return fa::ws_bytes((long long)B * H, N);
 }
 
-bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
-
 template <typename T>
 int fwd_checked(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d, float scale,
                 int causal, const uint8_t* block_mask, bool bf16, long long* elems) {
@@ -87,10 +87,9 @@ int bwd_checked(const T* q, const T* k, const T* v, const T* o, const T* dout, c
   int st = check_common(B, H, N, d, scale, causal, block_mask, bf16, elems);
   if (st != FA_OK) return st;
   if (!ws || ws_bytes < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  if (!aligned256(ws)) return FA_ERR_ALIGN;
   const long long tb = *elems * (long long)sizeof(T), lb = (long long)B * H * N * 4;
   const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   Range in[7] = {rng(q, tb),    rng(k, tb),   rng(v, tb), rng(o, tb), rng(dout, tb), rng(lse, lb),
@@ -138,7 +137,8 @@ fa::FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float
   a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   a.causal = causal;
   a.scale = scale;
-  a.scale_log2 = scale * fa::kLog2e;
+  a.scale_log2 = std::fabs(scale) * fa::kLog2e;
+  a.qsign = scale < 0.f ? 0x80008000u : 0u;
   a.splits = 1;
   return a;
 }
@@ -169,7 +169,8 @@ fa::BwdArgs stage_args(const void* q, const void* k, const void* v, const void* 
   a.nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   a.causal = causal;
   a.scale = scale;
-  a.scale_log2 = scale * fa::kLog2e;
+  a.scale_log2 = std::fabs(scale) * fa::kLog2e;
+  a.ssign = scale < 0.f ? 0x80008000u : 0u;
   return a;
 }
 
@@ -183,8 +184,8 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1; sizes must fit; mask blocks <= limit)";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
-    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "a tensor or workspace pointer is not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and nonzero";
     case FA_ERR_WORKSPACE: return "workspace is NULL or smaller than flash_attn_bwd_workspace_bytes()";
     case FA_ERR_HIP: return "a HIP kernel launch failed";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
@@ -222,7 +223,7 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   if (splits < 1 || splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   const size_t need = splitkv_workspace_bytes(B, H, N, d, splits);
   if (!workspace || workspace_bytes_ < need) return FA_ERR_WORKSPACE;
-  if (!aligned256(workspace)) return FA_ERR_ALIGN;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
   const long long tb = elems * 2, lb = (long long)B * H * N * 4;
   const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
   Range in[4] = {rng(q, tb), rng(k, tb), rng(v, tb), rng(block_mask, block_mask ? nb * nb : 0)};
@@ -288,7 +289,8 @@ int flash_attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* q_scales, const uint8
   a.BH = (int)bh;
   a.nb = (int)nb;
   a.causal = causal;
-  a.scale_log2 = scale * fa::kLog2e;
+  a.scale_log2 = std::fabs(scale) * fa::kLog2e;
+  a.qsign = scale < 0.f ? 0x80808080u : 0u;
   return status_of(fa::launch_fwd_mxfp8(a, stream));
 }
 
@@ -398,7 +400,6 @@ int flash_attn_bwd_preprocess(const void* q, const void* o, const void* dout, vo
   int st = stage_checked(in, ib, 3, out, ob, 1, B, H, N, d, 1.0f, 0, nullptr);
   if (st != FA_OK) return st;
   if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
-  if (!aligned256(workspace)) return FA_ERR_ALIGN;
   const fa::BwdArgs a = stage_args(q, nullptr, nullptr, o, dout, nullptr, workspace, nullptr, nullptr, nullptr, B, H,
                                    N, d, 1.0f, 0, nullptr);
   return status_of(fa::launch_bwd_delta_bf16(a, stream));
@@ -415,7 +416,6 @@ int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void*
   int st = stage_checked(in, ib, 6, out, ob, 2, B, H, N, d, scale, causal, block_mask);
   if (st != FA_OK) return st;
   if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
-  if (!aligned256(workspace)) return FA_ERR_ALIGN;
   const fa::BwdArgs a =
       stage_args(q, k, v, nullptr, dout, lse, workspace, nullptr, dk, dv, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_dkdv_bf16(a, stream));
@@ -432,7 +432,6 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
   int st = stage_checked(in, ib, 6, out, ob, 1, B, H, N, d, scale, causal, block_mask);
   if (st != FA_OK) return st;
   if (workspace_bytes_ < workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
-  if (!aligned256(workspace)) return FA_ERR_ALIGN;
   const fa::BwdArgs a =
       stage_args(q, k, v, nullptr, dout, lse, workspace, dq, nullptr, nullptr, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_dq_bf16(a, stream));

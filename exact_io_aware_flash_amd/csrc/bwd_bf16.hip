@@ -24,6 +24,9 @@
 //                 one block between the MFMAs of the other).
 // dQ is produced without atomics, so every output element is written once and results are
 // bitwise reproducible run to run.
+// A negative scale is folded into the sign of the operand each kernel holds in registers for S
+// (K in dK/dV, Q in dQ; exact in bf16), so P = exp2(|scale| log2(e) S' - LSE log2(e)) with
+// S' = sign(scale) Q K^T; dK and dQ are multiplied by the signed scale at the end.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_wave_kernel(BwdArgs a, Sched 
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     if (key < N) {
-      kreg[c] = *reinterpret_cast<const bf16x8*>(a.k + base + (size_t)key * D + 16 * c + 8 * h);
+      kreg[c] = xor_sign(*reinterpret_cast<const bf16x8*>(a.k + base + (size_t)key * D + 16 * c + 8 * h), a.ssign);
       vreg[c] = *reinterpret_cast<const bf16x8*>(a.v + base + (size_t)key * D + 16 * c + 8 * h);
     } else {
       kreg[c] = zero_bf16x8();
@@ -417,10 +420,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   // ---- this lane's key: its K (P wave) or V (dS wave) row as B operands (features 16c + 8h ..)
   const int key = k0w + c32;
   const __bf16* __restrict__ kvsrc = (dsw ? a.v : a.k) + base;
+  const uint32_t ksign = dsw ? 0u : a.ssign;  // the sign of scale rides on K (P wave only)
   bf16x8 kv[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c)
-    kv[c] = key < N ? *reinterpret_cast<const bf16x8*>(kvsrc + (size_t)key * D + 16 * c + 8 * h) : zero_bf16x8();
+    kv[c] = key < N ? xor_sign(*reinterpret_cast<const bf16x8*>(kvsrc + (size_t)key * D + 16 * c + 8 * h), ksign)
+                    : zero_bf16x8();
   f32x16 acc[DB];  // dV (P wave) or dK / scale (dS wave)
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = zero16();
@@ -815,7 +820,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     if (qrow < N) {
-      qreg[c] = *reinterpret_cast<const bf16x8*>(a.q + base + (size_t)qrow * D + 16 * c + 8 * h);
+      qreg[c] = xor_sign(*reinterpret_cast<const bf16x8*>(a.q + base + (size_t)qrow * D + 16 * c + 8 * h), a.ssign);
       doreg[c] = *reinterpret_cast<const bf16x8*>(a.dout + base + (size_t)qrow * D + 16 * c + 8 * h);
     } else {
       qreg[c] = zero_bf16x8();

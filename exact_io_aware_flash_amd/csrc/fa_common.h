@@ -43,6 +43,17 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
 }
 
+// XOR a per-dword mask into 8 packed bf16: with 0x80008000 every element changes sign (exact,
+// including zeros and NaN), with 0 nothing changes
+__device__ __forceinline__ bf16x8 xor_sign(bf16x8 x, uint32_t m) {
+  uint4 u = __builtin_bit_cast(uint4, x);
+  u.x ^= m;
+  u.y ^= m;
+  u.z ^= m;
+  u.w ^= m;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // ---------------------------------------------------------------------------------------------
 // LDS operand reads.  Row operands use 16-byte ds_read_b128 (LDS serves 16 lanes per pass over a
 // 256-byte bank window); operands that need the contraction index inside a lane use the 8-byte

@@ -17,8 +17,11 @@ struct FwdArgs {
   float* lse;
   const uint8_t* mask;  // nullptr = dense
   int N, d, BH, nb, causal;
-  float scale;       // natural-units scale
-  float scale_log2;  // scale * log2(e)
+  float scale;       // natural-units scale (either sign)
+  float scale_log2;  // |scale| * log2(e)
+  // sign of scale folded into the Q operand: 0x80008000 flips both bf16 of a dword (exact), 0
+  // leaves them; S = |scale| (sign * Q) K^T is then the scaled score for either sign
+  uint32_t qsign;
   // split-key forward: the 128-key blocks are cut into `splits` contiguous ranges (range s =
   // blocks [s * nb / splits, (s + 1) * nb / splits)); range s writes its normalised partial
   // output to o_part[s] (float32 [BH, N, d]) and its log-sum-exp to lse_part[s] ([BH, N])
@@ -48,7 +51,11 @@ struct BwdArgs {
   float* delta;  // workspace: D = rowsum(dO * O), [BH, N]
   const uint8_t* mask;
   int N, d, BH, nb, causal;
-  float scale, scale_log2;
+  float scale;       // signed: multiplies dK and dQ at the end
+  float scale_log2;  // |scale| * log2(e)
+  // sign of scale folded into the operand held in registers for S (Q in the dQ kernel, K in the
+  // dK/dV kernels): 0x80008000 per dword of bf16 pairs, or 0
+  uint32_t ssign;
 };
 
 // Backward workspace: delta (float32 [BH, N]), 256-byte aligned size.
@@ -116,7 +123,8 @@ struct Fp8FwdArgs {
   float* lse;
   const uint8_t* mask;
   int N, Np, d, BH, nb, causal;
-  float scale_log2;
+  float scale_log2;  // |scale| * log2(e)
+  uint32_t qsign;    // 0x80808080 flips the sign bit of four E4M3 Q codes (scale < 0), or 0
 };
 inline int fp8_vt_cols(int N) { return (N + 63) / 64 * 64; }
 

@@ -23,6 +23,7 @@
 //    from the row-major V tile with the transposing ds_read_b64_tr_b16.  K rows are read in a
 //    bit-permuted order that makes each lane's 8 P values 8 consecutive keys.  Both tiles use
 //    a 16-byte-chunk XOR swizzle that keeps their reads free of LDS bank conflicts.
+//  * a negative scale is folded into Q's sign (exact in bf16), so the exponent uses |scale|;
 //  * exponentials in base 2 with scale*log2(e) folded into one FMA; the running maximum is only
 //    moved when a new score exceeds it by more than 2^8, so most tiles skip the O rescale (the
 //    result is the same: numerator and denominator always share the offset).
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
   bf16x8 qreg[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c)
-    qreg[c] = qrow < N ? *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + 16 * c + 8 * h) : zero_bf16x8();
+    qreg[c] = qrow < N ? xor_sign(*reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + 16 * c + 8 * h), a.qsign)
+                       : zero_bf16x8();
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -201,6 +203,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
     update_max(sbuf[0], m_used, alpha);
     alpha = 1.f;  // nothing accumulated yet
   }
+  // every wave has read K[0] before step 0 copies K[2] over it (in later steps the barrier at
+  // the end of the previous step orders the read of K[t] before the copy of K[t+2])
+  if (ntiles > 2) lds_barrier();
 
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;  // t % 2

@@ -241,6 +241,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
         lo = *reinterpret_cast<const uint4*>(qr + 64 * f + 16 * h);
         hi4 = *reinterpret_cast<const uint4*>(qr + 64 * f + 32 + 16 * h);
       }
+      // a negative scale flips the sign bit of every Q code (exact), the exponent uses |scale|
+      const uint32_t m = a.qsign;
+      lo.x ^= m; lo.y ^= m; lo.z ^= m; lo.w ^= m;
+      hi4.x ^= m; hi4.y ^= m; hi4.z ^= m; hi4.w ^= m;
       qop[f] = join16x2(lo, hi4);
     }
     if (qrow < N) {
@@ -378,6 +382,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     update_max(sbuf[0], m_used, alpha);
     alpha = 1.f;  // nothing accumulated yet
   }
+  // every wave has read K[0] before step 0 copies K[2] over it
+  if (ntiles > 2) lds_barrier();
 
   auto step = [&](int t, auto parity) {
     constexpr int par = decltype(parity)::value;  // t % 2

@@ -13,7 +13,10 @@
  *               N x d matrix per batch b and head h, as in [P2 "A Worked Example in Pseudocode"]).
  *               LSE is a contiguous [B, H, N] float32 tensor.  All are device pointers, 16-byte
  *               aligned.  Offsets are computed in 64 bits.
- *   Scale       S = scale * Q K^T; scale must be finite and > 0 (usually 1/sqrt(d)).
+ *   Scale       S = scale * Q K^T; scale must be finite and nonzero, of either sign (usually
+ *               1/sqrt(d)).  A negative scale is applied exactly: the bf16 and FP8 kernels flip
+ *               the sign of the operand they hold in registers (exact) and use |scale| in the
+ *               exponent; the fp32 kernels scale each score before taking the row maximum.
  *   Causal      causal = 1 lets query i see key j only when j <= i (square, top-left aligned);
  *               causal = 0 lets every query see every key.
  *   Block mask  block_mask == NULL means dense.  Otherwise a device uint8 array [nb][nb],
@@ -54,8 +57,8 @@ enum {
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, a size overflows, or nb > FA_MAX_MASK_BLOCKS */
   FA_ERR_HEADDIM = 3,   /* d not in {64, 128} */
-  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (the workspace: 256-byte) */
-  FA_ERR_SCALE = 5,     /* scale not finite or not > 0 */
+  FA_ERR_ALIGN = 4,     /* a tensor or workspace pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 5,     /* scale not finite, or zero */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than flash_attn_bwd_workspace_bytes() */
   FA_ERR_HIP = 7,       /* a kernel launch failed */
   FA_ERR_ALIAS = 8,     /* an output overlaps an input or another output */
@@ -95,7 +98,7 @@ int flash_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
  *   q, k, v, o, lse, scale, causal, block_mask   as flash_attn_fwd
  *   splits      1 .. FA_MAX_SPLITS (else FA_ERR_SPLITS)
  *   workspace   at least flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) bytes,
- *               256-byte aligned, owned by the caller; holds the float32 partials
+ *               16-byte aligned, owned by the caller; holds the float32 partials
  *               ([splits, B, H, N, d] outputs, then [splits, B, H, N] log-sum-exps); contents
  *               undefined afterwards.  Must not overlap any input or output (FA_ERR_ALIAS).
  */
@@ -179,7 +182,7 @@ size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
  *   o, lse      in   the forward's outputs for the same inputs, scale, causal and block_mask
  *   dout        in   bf16 [B, H, N, d]  (dO)
  *   dq, dk, dv  out  bf16 [B, H, N, d]
- *   workspace   scratch of at least flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 256-byte
+ *   workspace   scratch of at least flash_attn_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
  *               aligned; its contents are undefined afterwards.
  */
 int flash_attn_bwd(const void *q, const void *k, const void *v, const void *o,

@@ -49,10 +49,11 @@ def check_brute_force(forward_head, seed=0):
         for d in (1, 3, 4):
             q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
             for causal in (False, True):
-                O, L = forward_head(q, k, v, 0.7, causal)
-                Ob, Lb = brute_force_head(q.tolist(), k.tolist(), v.tolist(), 0.7, causal)
-                assert np.abs(O - Ob).max() <= 1e-13, ("brute force O", N, d, causal)
-                assert np.abs(L - Lb).max() <= 1e-13, ("brute force LSE", N, d, causal)
+                for scale in (0.7, -0.7):  # a negative scale reverses which keys dominate
+                    O, L = forward_head(q, k, v, scale, causal)
+                    Ob, Lb = brute_force_head(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+                    assert np.abs(O - Ob).max() <= 1e-13, ("brute force O", N, d, causal, scale)
+                    assert np.abs(L - Lb).max() <= 1e-13, ("brute force LSE", N, d, causal, scale)
 
 
 def check_brute_force_masked(forward_head, seed=1):
@@ -213,7 +214,7 @@ def check_finite_differences(forward_head, backward_head, seed=10, h=1e-6):
              if not (N >= 8 and d >= 8 and not c)]
     for N, d, causal in cases:
         q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
-        scale = 0.75
+        scale = 0.75 if (N + d) % 2 else -0.75  # both signs of the scale
         dQ, dK, dV = backward_head(q, k, v, do, scale, causal, None)
         for name, X, G in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
             for idx in np.ndindex(*X.shape):

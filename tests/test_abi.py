@@ -85,11 +85,15 @@ def test_fwd_argument_errors(L, f32):
     assert fwd_call(L, q, k, v, o, lse, H=-1, f32=f32) == fa.FA_ERR_SHAPE
     for d in (0, 32, 96, 256):
         assert fwd_call(L, q, k, v, o, lse, d=d, f32=f32) == fa.FA_ERR_HEADDIM
-    for s in (0.0, -0.5, float("inf"), float("nan")):
+    for s in (0.0, -0.0, float("inf"), -float("inf"), float("nan")):
         assert fwd_call(L, q, k, v, o, lse, scale=s, f32=f32) == fa.FA_ERR_SCALE
     assert fwd_call(L, q, k, v, o, lse, causal=2, f32=f32) == fa.FA_ERR_FLAG
     mis = ctypes.c_void_p(q.value + 8)
     assert fwd_call(L, mis, k, v, o, lse, f32=f32) == fa.FA_ERR_ALIGN
+    # any finite nonzero scale passes validation, negative ones included: these calls get as far
+    # as the alignment check (so nothing is launched on the fake pointers)
+    for s in (-0.5, -1e-30, -3e38, 1e-30):
+        assert fwd_call(L, mis, k, v, o, lse, scale=s, f32=f32) == fa.FA_ERR_ALIGN
     # outputs aliasing inputs or each other
     assert fwd_call(L, q, k, v, q, lse, f32=f32) == fa.FA_ERR_ALIAS
     assert fwd_call(L, q, k, v, o, ctypes.c_void_p(o.value + 64), f32=f32) == fa.FA_ERR_ALIAS
@@ -106,6 +110,10 @@ def test_fwd_size_limits(L, f32):
     assert fwd_call(L, q, k, v, o, lse, B=1 << 16, H=1 << 15, N=1, f32=f32) == fa.FA_ERR_SHAPE
     assert fwd_call(L, q, k, v, o, lse, N=1 << 22, d=128, f32=f32) == fa.FA_ERR_SHAPE
     assert fwd_call(L, q, k, v, o, lse, B=1 << 15, H=1 << 15, N=256, f32=f32) == fa.FA_ERR_SHAPE
+    # B*H = 2^30 with N = 2^30: the per-head size check runs before any product that could
+    # leave 64 bits
+    assert fwd_call(L, q, k, v, o, lse, B=1 << 15, H=1 << 15, N=1 << 30, d=128, f32=f32) == fa.FA_ERR_SHAPE
+    assert fwd_call(L, q, k, v, o, lse, B=1 << 15, H=1 << 15, N=(1 << 31) - 1, d=128, f32=f32) == fa.FA_ERR_SHAPE
     if f32:
         assert fwd_call(L, q, k, v, o, lse, B=65536, H=1, N=1, f32=True) == fa.FA_ERR_SHAPE
 
@@ -128,7 +136,7 @@ def test_bwd_argument_errors(L, f32):
     p = ptrs(9)
     ws = ptrs(1, start=1 << 45)[0]
     need = fa.workspace_bytes(1, 1, 128, 64)
-    assert bwd_call(L, p, ctypes.c_void_p(ws.value + 16), need, f32=f32) == fa.FA_ERR_ALIGN
+    assert bwd_call(L, p, ctypes.c_void_p(ws.value + 8), need, f32=f32) == fa.FA_ERR_ALIGN
     assert bwd_call(L, p, None, need, f32=f32) == fa.FA_ERR_WORKSPACE
     assert bwd_call(L, p, ws, need - 1, f32=f32) == fa.FA_ERR_WORKSPACE
     for i in range(9):
@@ -136,11 +144,16 @@ def test_bwd_argument_errors(L, f32):
         pp[i] = None
         assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_NULL, i
     assert bwd_call(L, p, ws, need, d=80, f32=f32) == fa.FA_ERR_HEADDIM
-    assert bwd_call(L, p, ws, need, scale=-1.0, f32=f32) == fa.FA_ERR_SCALE
+    assert bwd_call(L, p, ws, need, scale=0.0, f32=f32) == fa.FA_ERR_SCALE
+    assert bwd_call(L, p, ws, need, scale=float("-inf"), f32=f32) == fa.FA_ERR_SCALE
     assert bwd_call(L, p, ws, need, causal=-1, f32=f32) == fa.FA_ERR_FLAG
     pp = list(p)
     pp[6] = pp[0]  # dq == q
     assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_ALIAS
+    # a negative scale and a workspace aligned to 16 bytes (not 256) pass validation: the call
+    # gets as far as the alias check
+    assert bwd_call(L, pp, ws, need, scale=-1.0, f32=f32) == fa.FA_ERR_ALIAS
+    assert bwd_call(L, pp, ctypes.c_void_p(ws.value + 16), need, f32=f32) == fa.FA_ERR_ALIAS
     pp = list(p)
     pp[7] = pp[8]  # dk == dv
     assert bwd_call(L, pp, ws, need, f32=f32) == fa.FA_ERR_ALIAS
@@ -165,7 +178,7 @@ def test_stage_argument_errors(L):
     assert L.flash_attn_bwd_preprocess(None, o, do, ws, need, *dims, None) == fa.FA_ERR_NULL
     assert L.flash_attn_bwd_preprocess(q, o, do, ws, need, 1, 1, 128, 32, None) == fa.FA_ERR_HEADDIM
     assert L.flash_attn_bwd_preprocess(q, o, do, ws, need - 1, *dims, None) == fa.FA_ERR_WORKSPACE
-    assert L.flash_attn_bwd_preprocess(q, o, do, ctypes.c_void_p(ws.value + 16), need, *dims,
+    assert L.flash_attn_bwd_preprocess(q, o, do, ctypes.c_void_p(ws.value + 8), need, *dims,
                                        None) == fa.FA_ERR_ALIGN
     assert L.flash_attn_bwd_preprocess(q, o, do, ctypes.c_void_p(o.value + 256), need, *dims,
                                        None) == fa.FA_ERR_ALIAS
@@ -180,6 +193,7 @@ def test_stage_argument_errors(L):
     a = list(args)
     a[8] = a[7]
     assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
+    assert L.flash_attn_bwd_dkdv(*a, *dims, -0.125, 0, None, None) == fa.FA_ERR_ALIAS
     a = list(args)
     a[7] = a[4]  # dk over lse
     assert L.flash_attn_bwd_dkdv(*a, *dims, 0.125, 0, None, None) == fa.FA_ERR_ALIAS
@@ -224,7 +238,10 @@ def test_splitkv_argument_errors(L):
     assert call(splits=fa.MAX_SPLITS + 1) == fa.FA_ERR_SPLITS
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
-    assert call(ws=ctypes.c_void_p(ws.value + 128)) == fa.FA_ERR_ALIGN
+    assert call(ws=ctypes.c_void_p(ws.value + 8)) == fa.FA_ERR_ALIGN
+    # a 16-byte aligned workspace and a negative scale pass validation (stopped by the alias check)
+    assert call(ws=ctypes.c_void_p(k.value + 16)) == fa.FA_ERR_ALIAS
+    assert call(scale=-0.125, o=q) == fa.FA_ERR_ALIAS
     assert call(ws=k) == fa.FA_ERR_ALIAS  # workspace over an input
     assert call(ws=ctypes.c_void_p(o.value + 256)) == fa.FA_ERR_ALIAS  # workspace over the output
     assert call(o=q) == fa.FA_ERR_ALIAS
@@ -270,10 +287,12 @@ def test_mxfp8_argument_errors(L):
     assert fwd8(N=0) == fa.FA_ERR_SHAPE
     assert fwd8(d=96) == fa.FA_ERR_HEADDIM
     assert fwd8(scale=0.0) == fa.FA_ERR_SCALE
+    assert fwd8(scale=float("nan")) == fa.FA_ERR_SCALE
     assert fwd8(causal=2) == fa.FA_ERR_FLAG
     a = list(base)
     a[2] = ctypes.c_void_p((1 << 40) + 2 * BIG + 8)
     assert fwd8(*a) == fa.FA_ERR_ALIGN
+    assert fwd8(*a, scale=-0.125) == fa.FA_ERR_ALIGN  # a negative scale passes validation
     a = list(base)
     a[6] = a[4]  # output over V's codes
     assert fwd8(*a) == fa.FA_ERR_ALIAS

@@ -189,6 +189,14 @@ def test_fwd_mxfp8_matches_oracle(dev, name, B, H, N, d, causal, dens):
     assert worst <= 1.0
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_mxfp8_negative_scale(dev, causal):
+    # a negative scale flips the sign of the Q codes (exact in E4M3)
+    t = workloads.random_case(1, 2, 700, 128, "bf16", seed=3050, with_do=False)
+    worst = _fp8_case("negative scale", t, -1.0 / np.sqrt(128), causal, dev, [(0, 0), (0, 1)])
+    assert worst <= 1.0
+
+
 def test_fwd_mxfp8_dead_rows(dev):
     # a block mask with an empty block row (non-causal): those queries see no key
     t = workloads.random_case(1, 2, 384, 64, "bf16", seed=3101, with_do=False)

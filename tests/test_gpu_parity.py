@@ -113,6 +113,32 @@ def test_ragged_multi_tile(dev, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mode", ["dense", "causal", "mask", "causal+mask"])
+def test_negative_scale(dev, d, dtype, mode):
+    """A negative scale (S = scale Q K^T reverses which keys dominate): forward and backward
+    against the oracle, one and several tiles, ragged tails."""
+    causal = "causal" in mode
+    for N in (63, 300, 1000):
+        t = workloads.random_case(1, 2, N, d, dtype, seed=1700 + N + d,
+                                  mask_density=0.6 if "mask" in mode else None, mask_seed=1800 + N)
+        if t.block_mask is not None:
+            np.fill_diagonal(t.block_mask, 1)
+        _run_and_compare(f"negative scale N={N} d={d} {dtype} {mode}", t, -1.0 / math.sqrt(d), causal, dev,
+                         heads=[(0, 0), (0, 1)])
+
+
+def test_negative_scale_long_sampled(dev):
+    """Negative scale on a long causal head (N = 8192, d = 128: many tiles, the running maximum
+    moving), sampled rows and key columns."""
+    t = workloads.random_case(1, 8, 8192, 128, "bf16", seed=1900)
+    rows = G.sample_rows(8192, 40, seed=1901)
+    cols = G.sample_rows(8192, 40, seed=1902)
+    _run_and_compare("negative scale N=8192 d=128", t, -1.0 / math.sqrt(128), True, dev, heads=[(0, 0), (0, 5)],
+                     rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_dead_rows(dev, dtype, d):
     """Rows that see no key: O = 0, LSE = -inf, no gradient (a zero mask row; and causal with a
     mask that only allows later blocks)."""
@@ -197,6 +223,38 @@ def test_non_default_stream(dev):
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
+def test_explicit_stream_argument(dev):
+    """stream= passed explicitly (not the current stream): the binding's internal temporaries
+    (the backward's workspace, the split-key partials) stay reserved for that stream while its
+    kernels run, though allocations and kernels on the current stream follow in between."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(2, 4, 2000, 128, "bf16", seed=710)
+    q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+    ref_o, ref_l = fa.fwd(q, k, v, 0.09, True)
+    ref_g = fa.bwd(q, k, v, ref_o, ref_l, do, 0.09, True)
+    ref_s = fa.fwd_splitkv(q, k, v, 0.09, True, None, 4)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    o, l = fa.fwd(q, k, v, 0.09, True, stream=s)
+    s.synchronize()
+    g = fa.bwd(q, k, v, o, l, do, 0.09, True, stream=s)
+    so = fa.fwd_splitkv(q, k, v, 0.09, True, None, 4, stream=s)
+    # allocations and writes on the current stream while the kernels on s may still run
+    junk = [torch.full((1 << 20,), 3.0, device=dev) for _ in range(8)]
+    for j in junk:
+        j.mul_(2.0)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
+    assert torch.equal(so[0], ref_s[0]) and torch.equal(so[1], ref_s[1])
+
+
 def test_invalid_call_leaves_outputs_untouched(dev):
     import ctypes
 
@@ -216,7 +274,7 @@ def test_invalid_call_leaves_outputs_untouched(dev):
     torch.cuda.synchronize()
     assert torch.all(o == 7.0) and torch.all(lse == 3.0)
     with pytest.raises(fa.FlashAttnError):
-        fa.fwd(q, q, q, scale=-1.0)
+        fa.fwd(q, q, q, scale=0.0)
 
 
 def test_backward_stages_equal_bwd(dev):
@@ -284,6 +342,19 @@ def test_splitkv_matches_oracle(dev, d, mode):
         torch.cuda.synchronize()
         assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
         G.compare_heads(t, {"o": o, "lse": lse}, 1.0 / math.sqrt(d), causal, heads=[(0, 0), (0, 1)], backward=False)
+
+
+def test_splitkv_negative_scale(dev):
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(1, 2, 1000, 128, "bf16", seed=1250, with_do=False)
+    q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+    for causal in (False, True):
+        o, lse = fa.fwd_splitkv(q, k, v, -0.1, causal, None, 3)
+        torch.cuda.synchronize()
+        G.compare_heads(t, {"o": o, "lse": lse}, -0.1, causal, heads=[(0, 0), (0, 1)], backward=False)
 
 
 def test_splitkv_long_head_sampled(dev):

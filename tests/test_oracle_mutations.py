@@ -47,6 +47,11 @@ def _scores_q_for_k(q, k, rows, scale, causal, bm):
     return np.where(vis, S, -np.inf)
 
 
+def _scores_abs_scale(q, k, rows, scale, causal, bm):
+    # the sign of the scale lost
+    return A._scores(q, k, rows, abs(scale), causal, bm)
+
+
 def _forward_log2_lse(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=1024):
     O, L = oracle.forward_head(q, k, v, scale, causal, block_mask, rows, chunk)
     return O, L / np.log(2.0)
@@ -58,6 +63,7 @@ FORWARD_MUTANTS = {
     "transposed block mask": _forward_with_scores(_scores_mask_transposed),
     "transposed operand": _forward_with_scores(_scores_q_for_k),
     "log2 statistic": _forward_log2_lse,
+    "sign of scale lost": _forward_with_scores(_scores_abs_scale),
 }
 
 
