@@ -1,8 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element.
 
 Tolerances: max-abs 1e-5 for fp32 inputs, 2e-2 for bf16 inputs (fp32 accumulation; for bf16
-outputs with |ref| >= 8 half a bf16 ulp of the value is added, the output's own storage
-rounding), 1e-3 for LSE.  Full-size workloads are run on the device in full; the oracle checks
+outputs half a bf16 ulp of the reference value is added, the output's own storage rounding),
+1e-3 for LSE.  Full-size workloads are run on the device in full; the oracle checks
 sampled heads, rows and key columns of them.
 """
 import math
