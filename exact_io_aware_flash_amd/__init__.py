@@ -27,6 +27,8 @@ FA_ERR_HIP = 7
 FA_ERR_ALIAS = 8
 FA_ERR_FLAG = 9
 FA_ERR_SPLITS = 10
+FA_ERR_SCRATCH = 11
+NOALLOC_MAX_ROWS = 1 << 22
 MASK_BLOCK = 128
 MAX_SPLITS = 64
 
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_mxfp8_quantize_vt.restype = i
     L.flash_attn_mxfp8_vt_cols.argtypes = [i]
     L.flash_attn_mxfp8_vt_cols.restype = ctypes.c_int64
+    L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_noalloc.restype = i
     L.flash_attn_status_string.argtypes = [i]
     L.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -205,6 +209,27 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, b
             _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, where)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float | None = None, causal: bool = False, block_mask=None,
+                stream=None):
+    """bf16 backward into caller-given dq, dk, dv through flash_attn_bwd_noalloc: the library's
+    fixed per-device scratch holds D, so neither the library nor this function allocates device
+    memory (B * H * N <= NOALLOC_MAX_ROWS).  Calls overlapping on one device race on the scratch."""
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), B, H, N, d, scale, int(bool(causal)), _ptr(bm), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_noalloc")
     return dq, dk, dv
 
 

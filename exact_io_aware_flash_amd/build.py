@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflash_attn.so")
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp8.hip", "bwd_bf16.hip", "f32.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_fp8.hip", "bwd_bf16.hip", "f32.hip", "noalloc.hip"]
 HEADERS = ["fa_common.h", "fa_kernels.h"]
 
 HIPCC_FLAGS = [

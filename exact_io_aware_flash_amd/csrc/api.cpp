@@ -11,6 +11,7 @@
 namespace {
 
 constexpr long long kMaxElems = (1LL << 62);
+static_assert(FA_NOALLOC_MAX_ROWS == fa::kNoallocMaxRows, "header and library agree on the fixed scratch");
 
 struct Range {
   uintptr_t lo, hi;
@@ -191,6 +192,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
     case FA_ERR_SPLITS: return "splits / parts must be in 1 .. FA_MAX_SPLITS";
+    case FA_ERR_SCRATCH: return "B * H * N exceeds FA_NOALLOC_MAX_ROWS, the fixed scratch of flash_attn_bwd_noalloc";
     default: return "unknown status";
   }
 }
@@ -357,6 +359,30 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                        workspace_bytes_, B, H, N, d, scale, causal, block_mask, true, &elems);
   if (st != FA_OK) return st;
   const fa::BwdArgs a = stage_args(q, k, v, o, dout, lse, workspace, dq, dk, dv, B, H, N, d, scale, causal, block_mask);
+  return status_of(fa::launch_bwd_bf16(a, stream));
+}
+
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int causal, const uint8_t* block_mask, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  long long elems = 0;
+  int st = check_common(B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * N > fa::kNoallocMaxRows) return FA_ERR_SCRATCH;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const long long tb = elems * 2, lb = (long long)B * H * N * 4;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[7] = {rng(q, tb),    rng(k, tb),   rng(v, tb), rng(o, tb), rng(dout, tb), rng(lse, lb),
+                 rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[3] = {rng(dq, tb), rng(dk, tb), rng(dv, tb)};
+  st = check_alias(in, 7, out, 3);
+  if (st != FA_OK) return st;
+  void* scratch = nullptr;  // this device's address of the library's fixed array
+  if (fa::noalloc_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  const fa::BwdArgs a = stage_args(q, k, v, o, dout, lse, scratch, dq, dk, dv, B, H, N, d, scale, causal, block_mask);
   return status_of(fa::launch_bwd_bf16(a, stream));
 }
 

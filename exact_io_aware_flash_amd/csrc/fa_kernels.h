@@ -61,6 +61,13 @@ struct BwdArgs {
 // Backward workspace: delta (float32 [BH, N]), 256-byte aligned size.
 inline size_t ws_bytes(long long BH, int N) { return ((size_t)BH * N * 4 + 255) & ~(size_t)255; }
 
+// Fixed device scratch of the allocation-free backward: float32 D for at most 2^22 query rows
+// (B * H * N), 16 MiB per device.  noalloc_scratch() returns the current device's address of the
+// array (looked up once per device); it allocates nothing.
+constexpr long long kNoallocMaxRows = 1LL << 22;
+constexpr size_t kNoallocScratchBytes = (size_t)kNoallocMaxRows * 4;
+hipError_t noalloc_scratch(void** out);
+
 struct F32Args {
   const float* q;
   const float* k;

@@ -63,7 +63,8 @@ enum {
   FA_ERR_HIP = 7,       /* a kernel launch failed */
   FA_ERR_ALIAS = 8,     /* an output overlaps an input or another output */
   FA_ERR_FLAG = 9,      /* causal not 0 or 1 */
-  FA_ERR_SPLITS = 10    /* splits / parts not in 1 .. FA_MAX_SPLITS */
+  FA_ERR_SPLITS = 10,   /* splits / parts not in 1 .. FA_MAX_SPLITS */
+  FA_ERR_SCRATCH = 11   /* B * H * N above FA_NOALLOC_MAX_ROWS (flash_attn_bwd_noalloc) */
 };
 
 /* Forward, bf16 inputs and outputs, fp32 accumulation.
@@ -229,6 +230,25 @@ int flash_attn_bwd_dq(const void *q, const void *k, const void *v, const void *d
                       void *dq,
                       int B, int H, int N, int d, float scale, int causal,
                       const uint8_t *block_mask, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc): flash_attn_bwd without the workspace argument.  The
+ * float32 rows of D it needs live in a fixed array inside the library, 16 MiB per device
+ * (FA_NOALLOC_MAX_ROWS rows), held from the first call on a device until the process ends; the
+ * call allocates and frees nothing.  Same kernels, results, arguments and checks as
+ * flash_attn_bwd otherwise.
+ *   B * H * N must be <= FA_NOALLOC_MAX_ROWS (else FA_ERR_SCRATCH, nothing enqueued).
+ *   Every call on one device shares that device's array: calls whose work overlaps on one device
+ *   (on different streams, or from different host threads without ordering) race on it and give
+ *   undefined results.  Calls ordered on one stream are safe; every row of D is rewritten by
+ *   each call before it is read, so nothing carries over from the previous call.
+ *   FA_ERR_HIP also reports a failed lookup of the array's device address. */
+#define FA_NOALLOC_MAX_ROWS 4194304
+int flash_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse,
+                           void *dq, void *dk, void *dv,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t *block_mask, hipStream_t stream);
 
 /* Static English text for a status code ("unknown status" for anything else). */
 const char *flash_attn_status_string(int status);

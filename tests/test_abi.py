@@ -303,3 +303,34 @@ def test_mxfp8_argument_errors(L):
         assert fn(x, c, sc, 1, 0, 128, 64, None) == fa.FA_ERR_SHAPE
         assert fn(x, x, sc, 1, 1, 128, 64, None) == fa.FA_ERR_ALIAS
         assert fn(x, ctypes.c_void_p((1 << 40) + BIG + 4), sc, 1, 1, 128, 64, None) == fa.FA_ERR_ALIGN
+
+
+def test_noalloc_argument_errors(L):
+    """flash_attn_bwd_noalloc refuses shapes beyond its fixed scratch (B * H * N rows) and every
+    other invalid argument before any HIP call, like flash_attn_bwd."""
+    import exact_io_aware_flash_amd as fa
+    p = ptrs(9)
+
+    def call(pp=p, B=1, H=1, N=128, d=64, scale=0.125, causal=0):
+        return L.flash_attn_bwd_noalloc(*pp, B, H, N, d, scale, causal, None, None)
+
+    assert fa.NOALLOC_MAX_ROWS == 1 << 22
+    assert call(B=1, H=1025, N=4096) == fa.FA_ERR_SCRATCH
+    assert call(B=2, H=1, N=(1 << 21) + 1) == fa.FA_ERR_SCRATCH
+    assert call(B=1 << 15, H=1 << 15, N=1 << 30, d=128) == fa.FA_ERR_SHAPE
+    for i in range(9):
+        pp = list(p)
+        pp[i] = None
+        assert call(pp) == fa.FA_ERR_NULL, i
+    assert call(d=96) == fa.FA_ERR_HEADDIM
+    assert call(scale=0.0) == fa.FA_ERR_SCALE
+    assert call(causal=3) == fa.FA_ERR_FLAG
+    pp = list(p)
+    pp[0] = ctypes.c_void_p(pp[0].value + 8)
+    assert call(pp) == fa.FA_ERR_ALIGN
+    pp = list(p)
+    pp[6] = pp[1]  # dq == k
+    assert call(pp) == fa.FA_ERR_ALIAS
+    # the largest accepted size and a negative scale pass the size and scale checks
+    assert call(pp, B=1, H=1024, N=4096, scale=-0.125) == fa.FA_ERR_ALIAS
+    assert "FA_NOALLOC_MAX_ROWS" in fa.status_string(fa.FA_ERR_SCRATCH)
