@@ -72,7 +72,7 @@ def preprocess_bytes(w):
     return 2 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
 
 
-KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "bwd_delta_kernel": "bwd_preprocess",
+KERNEL_KEYS = {"fwd_bf16_kernel": "fwd", "fwd_pingpong_kernel": "fwd_pingpong", "bwd_delta_kernel": "bwd_preprocess",
                "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dkdv_wave_kernel": "bwd_dkdv", "bwd_dq_kernel": "bwd_dq", "fwd_mxfp8_kernel": "fwd_mxfp8",
                "mx_quantize_rows_kernel": "mxfp8_quantize_rows", "mx_quantize_vt_kernel": "mxfp8_quantize_vt"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -85,6 +85,8 @@ def kernel_label(name: str):
         if key in name:
             if short == "fwd" and "<" in name and name.split("<", 1)[1].split(",")[1].strip() == "false":
                 return "fwd_noncausal"
+            if short == "fwd_pingpong" and "<false" in name:
+                return "fwd_pingpong_noncausal"
             return short
     return None
 
@@ -359,9 +361,11 @@ def percentiles(ms_list):
 
 
 def time_workload(fa, w, dev, steps: int, warmup: int):
-    """Forward and the three backward kernels of one workload on its seeded inputs, each bracketed
-    by events on torch's current stream (the stream the library launches on); medians over
-    `steps` steps, TFLOP/s under the same convention as the main figure."""
+    """Forward and the three backward kernels of one workload on its seeded inputs.  Each kernel
+    is launched `steps` times back to back (at least 20) between one pair of events on torch's
+    current stream (the stream the library launches on), so that the host's launch overhead of
+    these microsecond kernels stays out of the figure; TFLOP/s under the same convention as the
+    main figure."""
     import numpy as np
     import torch
 
@@ -380,21 +384,24 @@ def time_workload(fa, w, dev, steps: int, warmup: int):
              lambda: fa.bwd_preprocess(q, o, do, ws),
              lambda: fa.bwd_dkdv(q, k, v, do, lse, ws, w.scale, w.causal, mask, dk, dv),
              lambda: fa.bwd_dq(q, k, v, do, lse, ws, w.scale, w.causal, mask, dq)]
+    n = max(20, steps)
     for _ in range(warmup):
         for c in calls:
             c()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        for j, c in enumerate(calls):
+    per = []
+    for c in calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
             c()
-            ev[i][j + 1].record()
-    torch.cuda.synchronize()
-    per = [sorted(e[j].elapsed_time(e[j + 1]) for e in ev)[steps // 2] for j in range(len(calls))]
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
     ff = workloads.flops_fwd(B, H, N, d, w.causal, t.block_mask)
     fwd_ms, bwd_ms = per[0], sum(per[1:])
-    return {"config": w.description, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+    return {"config": w.description, "launches_per_kernel": n, "fwd_ms": fwd_ms, "bwd_preprocess_ms": per[1],
+            "bwd_dkdv_ms": per[2], "bwd_dq_ms": per[3], "bwd_ms": bwd_ms,
             "fwd_TFLOP/s": ff / (fwd_ms * 1e-3) / 1e12, "bwd_TFLOP/s": 2.5 * ff / (bwd_ms * 1e-3) / 1e12,
             "fwd+bwd_TFLOP/s": 3.5 * ff / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
 
@@ -452,28 +459,68 @@ def traffic_for(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(w, t, heads: int):
-    """The fp64 oracle timed on the host on `heads` heads of the same inputs (forward + backward)."""
+_CPU_T = None  # the workload's host tensors, shared with the forked oracle workers
+
+
+def _single_thread_blas():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _oracle_head(task):
+    """One (b, h) of the oracle in a worker process (forward, and backward unless forward-only)."""
     import numpy as np
 
     import oracle
     import workloads
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    f = lambda name, b, h: workloads.bf16_bits_to_f32(getattr(t, name)[b, h]).astype(np.float64)
+    b, h, scale, causal, fwd_only = task
+    f = lambda name: workloads.bf16_bits_to_f32(getattr(_CPU_T, name)[b, h]).astype(np.float64)
     t0 = time.perf_counter()
-    for i in range(heads):
-        b, h = divmod(i, w.H)
-        q, k, v, do = f("q", b, h), f("k", b, h), f("v", b, h), f("do", b, h)
-        oracle.forward_head(q, k, v, w.scale, w.causal, t.block_mask)
-        if not w.fwd_only:
-            oracle.backward_head(q, k, v, do, w.scale, w.causal, t.block_mask)
+    q, k, v = f("q"), f("k"), f("v")
+    oracle.forward_head(q, k, v, scale, causal, _CPU_T.block_mask)
+    if not fwd_only:
+        oracle.backward_head(q, k, v, f("do"), scale, causal, _CPU_T.block_mask)
+    return time.perf_counter() - t0
+
+
+def cpu_workers() -> int:
+    """Host cores this process may use (its CPU affinity), at most 16 (one GPU's share of a box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(w, t, heads: int | None = None):
+    """The fp64 oracle timed on the host: a pool of one process per usable core (BLAS limited to
+    one thread each), one (b, h) per task, `heads` heads of the same inputs (default: one per
+    worker), forward + backward.  Run before the GPU is initialised, and the pool is joined, so
+    no process outlives it."""
+    import multiprocessing
+
+    global _CPU_T
+    workers = cpu_workers()
+    heads = min(heads or workers, w.B * w.H)
+    tasks = [(i // w.H, i % w.H, w.scale, w.causal, w.fwd_only) for i in range(heads)]
+    _CPU_T = t
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    pool = ctx.Pool(workers, initializer=_single_thread_blas)
+    try:
+        per_head = pool.map(_oracle_head, tasks, chunksize=1)
+    finally:
+        pool.close()
+        pool.join()
     dt = time.perf_counter() - t0
+    _CPU_T = None
+    import workloads
+
     one = workloads.flops_fwd(1, 1, w.N, w.d, w.causal, t.block_mask)
     flops = heads * (one if w.fwd_only else 3.5 * one)
     cpu = platform.processor() or ""
@@ -488,10 +535,12 @@ def cpu_baseline(w, t, heads: int):
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{heads} of {w.B * w.H} heads (b,h)=(0,0).. of the same workload, fp64 numpy "
-                  f"{'forward' if w.fwd_only else 'forward+backward'}, {dt:.1f} s, {cpu}",
+        "sample": f"{heads} of {w.B * w.H} heads (b,h) of the same workload, fp64 numpy "
+                  f"{'forward' if w.fwd_only else 'forward+backward'}, one head per task on a pool of "
+                  f"{workers} processes with one BLAS thread each; {dt:.1f} s wall "
+                  f"(per head {min(per_head):.1f}-{max(per_head):.1f} s), {cpu}",
         "seconds": dt,
     }
 
@@ -555,7 +604,8 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the MX-FP8 forward figure")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads the oracle times on the host (default: one per usable core, at most 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="copy MIB MiB with the runtime's copy kernel before the bench (counter scaling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -618,6 +668,14 @@ def main():
         return
     t_gen = time.perf_counter()
     t = workloads.make(w, with_do=not w.fwd_only)
+    # the oracle on the host cores first, before anything initialises the GPU: its worker
+    # processes are forked from a process without GPU state and are all joined here
+    cpu_line = fp8_cpu_line = None
+    if not args.no_cpu_baseline and not args.data_sensitivity:
+        cpu_line = cpu_baseline(w, t, args.cpu_heads or None)
+        if not args.no_fp8:
+            fp8_cpu_line = fp8_cpu_baseline(w, t)
+        print(f"# cpu baseline done in {cpu_line['seconds']:.1f}s", file=sys.stderr, flush=True)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to_dev(t.q), to_dev(t.k), to_dev(t.v)
     do = to_dev(t.do) if not w.fwd_only else None
@@ -730,6 +788,31 @@ def main():
         ms_nc = e[0].elapsed_time(e[1]) / max(3, args.steps // 2)
         tf_nc = fnc / (ms_nc * 1e-3) / 1e12
         line["fwd_noncausal"] = {"ms": ms_nc, "TFLOP/s": tf_nc, "frac_of_peak": tf_nc / PEAK_BF16_TFLOPS}
+    if d == 128 and mask is None:
+        # the wave-specialised schedule beside the in-wave interleave of the metric's forward: both
+        # timed the same way (back-to-back calls between one event pair), alternating, same inputs
+        n_pp = max(5, args.steps)
+        def back_to_back(fn):
+            for _ in range(2):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(n_pp):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n_pp
+        pp, il = [], []
+        for _ in range(2):
+            pp.append(back_to_back(lambda: fa.fwd_pingpong(q, k, v, w.scale, w.causal, out=o, lse=lse)))
+            il.append(back_to_back(lambda: fa.fwd(q, k, v, w.scale, w.causal, None, out=o, lse=lse)))
+        pp_ms, il_ms = min(pp), min(il)
+        line["pingpong_forward"] = {"ms": pp_ms, "TFLOP/s": ff / (pp_ms * 1e-3) / 1e12,
+                                    "frac_of_peak": ff / (pp_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                    "interleave_ms": il_ms, "interleave_TFLOP/s": ff / (il_ms * 1e-3) / 1e12,
+                                    "pingpong_over_interleave_time": pp_ms / il_ms,
+                                    "schedule": "waves w and w+4 of each SIMD alternate matrix and softmax phases"}
     if args.workload == "long" and not args.no_other_workloads:
         # the other bf16 workloads (d = 64), each timed kernel by kernel the same way
         line["other_workloads"] = {n: time_workload(fa, workloads.WORKLOADS[n], dev, max(5, args.steps // 2), 2)
@@ -740,10 +823,10 @@ def main():
         line["library_gemm"] = library_gemm(dev)
     if not args.no_fp8:
         line["mxfp8_forward"] = fp8_forward(fa, w, q, k, v, mask, ff, max(3, args.steps))
-        if not args.no_cpu_baseline:
-            line["mxfp8_forward"]["cpu_baseline"] = fp8_cpu_baseline(w, t)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_heads)
+        if fp8_cpu_line:
+            line["mxfp8_forward"]["cpu_baseline"] = fp8_cpu_line
+    if cpu_line:
+        line["cpu_baseline"] = cpu_line
     print(json.dumps(line), flush=True)
 
 

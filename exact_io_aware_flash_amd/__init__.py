@@ -28,6 +28,7 @@ FA_ERR_ALIAS = 8
 FA_ERR_FLAG = 9
 FA_ERR_SPLITS = 10
 FA_ERR_SCRATCH = 11
+FA_ERR_UNSUPPORTED = 12
 NOALLOC_MAX_ROWS = 1 << 22
 MASK_BLOCK = 128
 MAX_SPLITS = 64
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_mxfp8_quantize_vt.restype = i
     L.flash_attn_mxfp8_vt_cols.argtypes = [i]
     L.flash_attn_mxfp8_vt_cols.restype = ctypes.c_int64
+    L.flash_attn_fwd_pingpong.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_fwd_pingpong.restype = i
     L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_bwd_noalloc.restype = i
     L.flash_attn_status_string.argtypes = [i]
@@ -171,6 +174,28 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_mask=No
             _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, where)
+    return out, lse
+
+
+def fwd_pingpong(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None, stream=None):
+    """Forward (bf16, d = 128, no block mask) with the wave-specialised schedule; bitwise the
+    same outputs as fwd().  Returns (o, lse)."""
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with _on(stream):
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    st = lib().flash_attn_fwd_pingpong(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                       int(bool(causal)), None, _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_pingpong")
     return out, lse
 
 

@@ -192,6 +192,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
     case FA_ERR_SPLITS: return "splits / parts must be in 1 .. FA_MAX_SPLITS";
+    case FA_ERR_UNSUPPORTED: return "option not supported by this entry point (see its declaration)";
     case FA_ERR_SCRATCH: return "B * H * N exceeds FA_NOALLOC_MAX_ROWS, the fixed scratch of flash_attn_bwd_noalloc";
     default: return "unknown status";
   }
@@ -209,6 +210,17 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
   int st = fwd_checked(qb, kb, vb, ob, lse, B, H, N, d, scale, causal, block_mask, true, &elems);
   if (st != FA_OK) return st;
   return status_of(fa::launch_fwd_bf16(fwd_args(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask), stream));
+}
+
+int flash_attn_fwd_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                            int d, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  long long elems = 0;
+  int st = fwd_checked(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                       static_cast<__bf16*>(o), lse, B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  if (d != 128 || block_mask) return FA_ERR_UNSUPPORTED;
+  return status_of(
+      fa::launch_fwd_pingpong_bf16(fwd_args(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask), stream));
 }
 
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int splits) {

@@ -136,6 +136,8 @@ struct Fp8FwdArgs {
 inline int fp8_vt_cols(int N) { return (N + 63) / 64 * 64; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// the wave-specialised forward (d = 128, no block mask, no split)
+hipError_t launch_fwd_pingpong_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_mxfp8(const Fp8FwdArgs& a, hipStream_t stream);
 // MX-FP8 quantisation of bf16 rows (blocks of 32 along d), and of V into the transposed layout
 hipError_t launch_mxfp8_quantize_rows(const __bf16* x, uint8_t* codes, uint8_t* scales, long long rows, int d,

@@ -38,13 +38,19 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
-  constexpr int BR = 128, BC = 64;
+
+// NW waves of 32 query rows each: BR = 32 NW rows per workgroup.  NW = 4 gives 128-row blocks
+// (one mask block; two or three workgroups per CU); NW = 8 gives 256-row blocks with one
+// workgroup per CU, so each K/V tile copied into LDS serves twice the query rows (half the
+// L2 -> LDS copy traffic per flop).  Block-sparse masks need NW = 4.
+template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(FwdArgs a, Sched sc) {
+  static_assert(NW == 4 || (NW == 8 && !SPARSE), "block-sparse masks need 128-row blocks");
+  constexpr int BR = 32 * NW, BC = 64;
   constexpr int DC = D / 16;  // 16-wide contraction chunks over d
   constexpr int DB = D / 32;  // 32-row output blocks over d
-  using KT = DmaTile<BC, D>;  // K rows, read 16 bytes per lane
-  using VT = DmaTile<BC, D>;  // V rows, read transposed (ds_read_b64_tr_b16)
+  using KT = DmaTile<BC, D, NW>;  // K rows, read 16 bytes per lane
+  using VT = DmaTile<BC, D, NW>;  // V rows, read transposed (ds_read_b64_tr_b16)
 
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT::BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[KT::BYTES];
@@ -355,6 +361,260 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16_kernel(FwdArgs 
 
 
 // ---------------------------------------------------------------------------------------------
+// Wave-specialised forward ("ping-pong"), d = 128: the matrix work and the softmax of the pages'
+// loop ([P2] "The Trick: Online Softmax") run in alternating phases on the two waves that share a
+// SIMD, so that one wave's MFMAs overlap the other wave's exponentials (the interleaving of matrix
+// products and softmax that "How FlashAttention Bypasses the GPU Memory Bottleneck to Enable
+// Long-Context AI" credits for FlashAttention-3's throughput, here across the two waves of a
+// SIMD instead of across warpgroups).
+//
+// One workgroup of 8 waves owns 256 query rows (32 per wave, Q^T held in registers as in
+// fwd_bf16_kernel).  Waves w and w + 4 run on the same SIMD; wave group g = w / 4.  Every wave
+// runs the same sequence of phases over its key tiles j = 0 .. T - 1 (64 keys each), one barrier
+// after each phase:
+//   M_j (matrix phase):  S[j] = K[j] Q^T (when j < T), O += V[j-1] P[j-1] (when j >= 1)
+//   V_j (softmax phase): mask S[j], running max, rescale O, P[j] = exp2(S[j] - m), row sums
+//   M_0 V_0 M_1 V_1 ... V_{T-1} M_T
+// but group 1 starts one phase later (an idle phase first; group 0 ends with one), so in every
+// phase one wave of each SIMD issues MFMAs while its partner issues the VALU work.  The matrix
+// phase runs at raised wave priority (s_setprio), so its MFMAs issue first when both waves are
+// ready.  K and V tiles are triple-buffered: K[j + 2] and V[j + 1] go into the buffers of K[j - 1]
+// and V[j - 2], which group 1 last reads in global phase 2j - 1, and are first read in phase
+// 2j + 4.  Each wave copies its share in global phase 2j (group 0 at the start of M_j, group 1 at
+// the start of V_{j-1}) and waits for its previous share at the end of each V phase.
+// Reached through flash_attn_fwd_pingpong; flash_attn_fwd keeps the in-wave interleave, which
+// times faster on MI355X: here all operand reads of a tile fall into the matrix phase of each
+// SIMD pair instead of spreading over the whole step.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched sc) {
+  constexpr int D = 128, NW = 8, BR = 32 * NW, BC = 64;
+  constexpr int DC = D / 16, DB = D / 32;
+  using KT = DmaTile<BC, D, NW>;
+
+  __shared__ __attribute__((aligned(1024))) char kbuf[3][KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[3][KT::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+            c32 = lane & 31;
+  const int grp = w >> 2;
+  const int N = a.N;
+  int bh, qt;
+  sched_decode(sc, gridDim.x, bh, qt);
+  const int q0 = qt * BR;
+  const size_t base = (size_t)bh * N * D;
+  const __bf16* __restrict__ Q = a.q + base;
+  const __bf16* __restrict__ K = a.k + base;
+  const __bf16* __restrict__ V = a.v + base;
+  int T = (N + BC - 1) / BC;
+  if (CAUSAL) T = min(T, (min(q0 + BR, N) - 1) / BC + 1);
+
+  const int qrow = q0 + 32 * w + c32;
+  bf16x8 qreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+    qreg[c] = qrow < N ? xor_sign(*reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + 16 * c + 8 * h), a.qsign)
+                       : zero_bf16x8();
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = zero16();
+  float m_used = neg_inf(), lsum = 0.f;
+  const float sl = a.scale_log2;
+
+  int kaddr[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) kaddr[c] = KT::off(perm32(c32), 16 * c + 8 * h);
+  int vaddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vaddr[u][db] = KT::off4(8 * h + 4 * u + (j >> 2), 32 * db + 16 * g + 4 * (j & 3));
+  }
+  KT kdma, vdma;
+  kdma.init(w, lane);
+  vdma.init(w, lane);
+
+  f32x16 s[2];   // S[j] of this wave's 32 queries: register r of half h holds key 64 j + 32 kb + acc_row(r, h)
+  bf16x8 pk[4];  // P[j] as the PV B operand: pk[m] holds keys 64 j + 16 m + 8h + 0..7
+#pragma unroll
+  for (int m = 0; m < 4; ++m) pk[m] = zero_bf16x8();
+
+  // matrix phase: 16 score MFMAs (HS) then 16 PV MFMAs (HP), each operand read from LDS four
+  // MFMAs ahead of its use
+  auto mphase = [&](auto hsc, auto hpc, const char* kb_, const char* vb_) __attribute__((always_inline)) {
+    constexpr bool HS = decltype(hsc)::value, HP = decltype(hpc)::value;
+    constexpr int I0 = HS ? 0 : 16, I1 = HP ? 32 : 16;
+    auto rd = [&](int i) -> bf16x8 {
+      if (i < 16) return lds_b128(kb_ + kaddr[i >> 1] + 32 * (i & 1) * D * 2);
+      const int db = (i - 16) >> 2, m = (i - 16) & 3;
+      const char* vb = vb_ + 16 * m * D * 2;
+      return join8(lds_tr4(vb + vaddr[0][db]), lds_tr4(vb + vaddr[1][db]));
+    };
+    __builtin_amdgcn_s_setprio(1);
+    if (HS) {
+      s[0] = zero16();
+      s[1] = zero16();
+    }
+    bf16x8 op[32];
+#pragma unroll
+    for (int i = I0; i < I0 + 4 && i < I1; ++i) op[i] = rd(i);
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+      if (i + 4 < I1) op[i + 4] = rd(i + 4);
+      if (i < 16)
+        s[i & 1] = mfma32(op[i], qreg[i >> 1], s[i & 1]);
+      else
+        oacc[(i - 16) >> 2] = mfma32(op[i], pk[(i - 16) & 3], oacc[(i - 16) >> 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // softmax phase of tile j: masks, running maximum (moved only past a 2^8 margin, as in
+  // fwd_bf16_kernel), rescale of O, P = exp2(S scale log2(e) - m) in fp32 for the row sums and
+  // as bf16 for PV
+  auto vphase = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BC;
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (CAUSAL) {
+          const int thr = min(qrow, N - 1) - (k0 + 32 * kb + 8 * h);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = acc_row(r, 0) > thr ? neg_inf() : s[kb][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + 32 * kb + acc_row(r, h) >= N) s[kb][r] = neg_inf();
+        }
+      }
+    }
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmax_nan(mt, s[kb][r]);
+    mt = half_swap_max(mt) * sl;
+    const float m_new = (mt > m_used + kRescaleThreshold) ? mt : m_used;
+    const float alpha = (m_new == m_used) ? 1.f : fast_exp2(m_used - m_new);
+    m_used = m_new;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      lsum *= alpha;
+    }
+    const float msub = (m_used == neg_inf()) ? 0.f : m_used;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+      const float p = fast_exp2(__builtin_fmaf(s[jj >> 4][jj & 15], sl, -msub));
+      part[jj & 3] += p;
+      pk[jj >> 3][jj & 7] = (__bf16)p;
+    }
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+  };
+  // this wave's share of the copies of K[i] and V[i - 1] into buffers i % 3 and (i - 1) % 3 (tiles
+  // past the end are skipped); returns the copy instructions issued
+  auto prefetch = [&](int i, auto rc) -> int {
+    constexpr int r = decltype(rc)::value;  // i % 3
+    int n = 0;
+    if (i < T) {
+      kdma.issue(K, N, kbuf[r], i * BC, w);
+      n += KT::CH;
+    }
+    if (i - 1 < T) {
+      vdma.issue(V, N, vbuf[(r + 2) % 3], (i - 1) * BC, w);
+      n += KT::CH;
+    }
+    return n;
+  };
+  // end of a softmax phase: the previous batch of this wave's copies has landed (the latest, n
+  // instructions, may stay in flight); then the barrier that publishes them
+  auto vphase_end = [&](int n) {
+    if (n == 2 * KT::CH)
+      wait_vm<2 * KT::CH>();
+    else if (n == KT::CH)
+      wait_vm<KT::CH>();
+    else
+      wait_vm<0>();
+    lds_barrier();
+  };
+  auto phase_end = []() { asm volatile("s_barrier" ::: "memory"); };
+
+  // unit j (buffers j % 3 fixed at compile time): M_j, then V_j when j < T.  Group 0 copies K[j+2]
+  // and V[j+1] as it starts M_j; group 1 copies K[j+3] and V[j+2] as it starts V_j.
+  auto unit = [&](int j, auto rc, auto hsc, auto hpc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    constexpr bool HS = decltype(hsc)::value;
+    int n = 0;
+    if (grp == 0) n = prefetch(j + 2, std::integral_constant<int, (r + 2) % 3>{});
+    mphase(hsc, hpc, kbuf[r], vbuf[(r + 2) % 3]);
+    phase_end();
+    if (HS) {
+      if (grp != 0) n = prefetch(j + 3, std::integral_constant<int, r>{});
+      vphase(j);
+      vphase_end(n);
+    }
+  };
+
+  // prologue: K[0], K[1], V[0] by every wave, and group 1's share of K[2], V[1] (group 0 copies
+  // its share at the start of M_0); then group 1's idle phase
+  kdma.issue(K, N, kbuf[0], 0, w);
+  if (T > 1) kdma.issue(K, N, kbuf[1], BC, w);
+  vdma.issue(V, N, vbuf[0], 0, w);
+  wait_vm<0>();
+  lds_barrier();
+  if (grp != 0) {
+    const int n = prefetch(2, std::integral_constant<int, 2>{});
+    (void)n;
+    phase_end();
+  }
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using Y = std::true_type;
+  using F = std::false_type;
+  unit(0, I0{}, Y{}, F{});
+  int j = 1;
+  for (; j + 2 < T; j += 3) {
+    unit(j, I1{}, Y{}, Y{});
+    unit(j + 1, I2{}, Y{}, Y{});
+    unit(j + 2, I0{}, Y{}, Y{});
+  }
+  if (j < T) {  // j % 3 == 1 here; at most two full units remain before unit T
+    unit(j, I1{}, Y{}, Y{});
+    ++j;
+    if (j < T) {
+      unit(j, I2{}, Y{}, Y{});
+      ++j;
+    }
+  }
+  switch (T % 3) {  // unit T: the last PV only
+    case 0: unit(T, I0{}, F{}, Y{}); break;
+    case 1: unit(T, I1{}, F{}, Y{}); break;
+    default: unit(T, I2{}, F{}, Y{}); break;
+  }
+  if (grp == 0) phase_end();  // group 0's idle phase at the end
+
+  const float ltot = half_swap_sum(lsum);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (qrow < N) {
+    __bf16* orow = a.o + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = v4;
+      }
+    if (h == 0) a.lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m_used + __log2f(ltot)) * kLn2 : neg_inf();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Log-sum-exp merge of partial results over disjoint key sets of the same query rows: with
 // LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s, which is the softmax over the union
 // of the key sets (each O_s is already normalised by its own sum).  Rows whose parts are all
@@ -393,12 +653,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 
 template <int D, bool C, bool S>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  constexpr int BR = 128;
+  constexpr int NW = (D == 128 && !S) ? 8 : 4;  // 256-row blocks at d = 128 (1-2% faster than 128-row)
+  constexpr int BR = 32 * NW;
   const int nq = (a.N + BR - 1) / BR;
-  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S>));
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S, false, NW>), 64 * NW);
   const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S, false, NW>), dim3(nq * a.BH), dim3(64 * NW), 0, st, a, sc);
   return hipGetLastError();
+}
+
+template <bool C>
+static hipError_t launch_pingpong_t(const FwdArgs& a, hipStream_t st) {
+  const int nq = (a.N + 255) / 256;
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_pingpong_kernel<C>), 512);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  hipLaunchKernelGGL((fwd_pingpong_kernel<C>), dim3(nq * a.BH), dim3(512), 0, st, a, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_pingpong_bf16(const FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_pingpong_t<true>(a, stream) : launch_pingpong_t<false>(a, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {

@@ -64,7 +64,8 @@ enum {
   FA_ERR_ALIAS = 8,     /* an output overlaps an input or another output */
   FA_ERR_FLAG = 9,      /* causal not 0 or 1 */
   FA_ERR_SPLITS = 10,   /* splits / parts not in 1 .. FA_MAX_SPLITS */
-  FA_ERR_SCRATCH = 11   /* B * H * N above FA_NOALLOC_MAX_ROWS (flash_attn_bwd_noalloc) */
+  FA_ERR_SCRATCH = 11,  /* B * H * N above FA_NOALLOC_MAX_ROWS (flash_attn_bwd_noalloc) */
+  FA_ERR_UNSUPPORTED = 12 /* an option the entry point does not support (flash_attn_fwd_pingpong) */
 };
 
 /* Forward, bf16 inputs and outputs, fp32 accumulation.
@@ -81,6 +82,21 @@ enum {
 int flash_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                    int B, int H, int N, int d, float scale, int causal,
                    const uint8_t *block_mask, hipStream_t stream);
+
+/* Forward, bf16, with the wave-specialised ("ping-pong") schedule instead of the in-wave
+ * interleave of flash_attn_fwd: the two waves that share each SIMD alternate between a phase of
+ * matrix products (S = K Q^T of one key tile, O += P V of the previous one) and a phase of softmax
+ * work (masks, running maximum, rescale, exponentials, row sums), one barrier per phase, so one
+ * wave's MFMAs run beside the other's VALU work.  This is the interleaving of matrix products and
+ * softmax that "How FlashAttention Bypasses the GPU Memory Bottleneck to Enable Long-Context AI"
+ * credits for FlashAttention-3's throughput, done across the two waves of a SIMD.  Same
+ * definition, arguments and results as flash_attn_fwd (the same products and sums in the same
+ * order: bitwise equal outputs); only d = 128 without a block mask (else FA_ERR_UNSUPPORTED).
+ * On MI355X it measures slower than flash_attn_fwd (the operand reads of a whole tile then fall
+ * into one phase of each SIMD pair); it is kept as the measured alternative schedule. */
+int flash_attn_fwd_pingpong(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int N, int d, float scale, int causal,
+                            const uint8_t *block_mask, hipStream_t stream);
 
 /* Forward with float32 inputs, outputs and arithmetic (no reduced-precision products).
  * Same definition and arguments as flash_attn_fwd with float tensors. */

@@ -334,3 +334,18 @@ def test_noalloc_argument_errors(L):
     # the largest accepted size and a negative scale pass the size and scale checks
     assert call(pp, B=1, H=1024, N=4096, scale=-0.125) == fa.FA_ERR_ALIAS
     assert "FA_NOALLOC_MAX_ROWS" in fa.status_string(fa.FA_ERR_SCRATCH)
+
+
+def test_pingpong_argument_errors(L):
+    """flash_attn_fwd_pingpong: flash_attn_fwd's checks, then d = 128 without a block mask only."""
+    import exact_io_aware_flash_amd as fa
+    q, k, v, o, lse, m = ptrs(6)
+
+    def call(d=128, mask=None, scale=0.125, o=o):
+        return L.flash_attn_fwd_pingpong(q, k, v, o, lse, 1, 1, 256, d, scale, 0, mask, None)
+
+    assert call(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(mask=m) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=96) == fa.FA_ERR_HEADDIM
+    assert call(scale=0.0) == fa.FA_ERR_SCALE
+    assert call(o=q) == fa.FA_ERR_ALIAS

@@ -36,6 +36,10 @@ def test_kernel_labels(bench):
     assert lab("void fa::(anonymous namespace)::fwd_mxfp8_kernel<128, true, false>(fa::Fp8FwdArgs, fa::Sched)") == \
         "fwd_mxfp8"
     assert lab("_ZN2fa12_GLOBAL__N_121mx_quantize_vt_kernelILi128EEEvPKDF16bPhS4_ii") == "mxfp8_quantize_vt"
+    assert lab("void fa::(anonymous namespace)::fwd_bf16_kernel<128, true, false, false, 8>(fa::FwdArgs, fa::Sched)") == "fwd"
+    assert lab("void fa::(anonymous namespace)::fwd_pingpong_kernel<true>(fa::FwdArgs, fa::Sched)") == "fwd_pingpong"
+    assert lab("void fa::(anonymous namespace)::fwd_pingpong_kernel<false>(fa::FwdArgs, fa::Sched)") == \
+        "fwd_pingpong_noncausal"
     assert lab("__amd_rocclr_copyBuffer") is None
 
 
@@ -154,3 +158,17 @@ def test_counters_from_shares_of_wave_cycles(bench, tmp_path):
     assert table[0].startswith("| kernel | dispatches | SQ_LDS_BANK_CONFLICT | SQ_WAIT_ANY | SQ_WAVE_CYCLES |")
     line = [l for l in table if l.startswith("| bwd_dkdv")][0]
     assert "| 2 |" in line and "250 (25.0%)" in line and "| 1000 |" in line
+
+
+def test_cpu_baseline_pool_joins(bench):
+    """The host oracle runs on a process pool (one (b, h) per task) and leaves no child process."""
+    import multiprocessing
+
+    import workloads
+
+    w = workloads.Workload("pool", 1, 3, 96, 64, "bf16", True, 77, 0.125, description="pool test")
+    t = workloads.make(w, with_do=True)
+    r = bench.cpu_baseline(w, t, heads=3)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["value"] > 0
+    assert "3 of 3 heads" in r["sample"]
+    assert multiprocessing.active_children() == []

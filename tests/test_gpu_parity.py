@@ -317,6 +317,44 @@ def test_autograd_wrapper(dev):
     G.compare_heads(t, res, 0.125, True, heads=[(0, 0), (0, 1)])
 
 
+# ------------------------------------------------------------------------------ wave-specialised forward
+@pytest.mark.parametrize("causal", [False, True])
+def test_pingpong_forward_equals_fwd_and_oracle(dev, causal):
+    """The wave-specialised forward computes the same products and sums in the same order as the
+    interleaved one: bitwise equal outputs; and both match the oracle (ragged N from one tile to
+    several, both signs of the scale)."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    for N, scale in ((1, 0.09), (65, 0.09), (300, -0.09), (1000, 0.09), (2049, 0.11)):
+        G.say(f"[case] pingpong N={N} causal={causal} scale={scale}")
+        t = workloads.random_case(2, 2, N, 128, "bf16", seed=2900 + N, with_do=False)
+        q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+        nan = lambda shape, dt: torch.full(shape, float("nan"), dtype=dt, device=dev)
+        o, lse = fa.fwd_pingpong(q, k, v, scale, causal, out=nan(q.shape, q.dtype), lse=nan(q.shape[:3], torch.float32))
+        o2, lse2 = fa.fwd(q, k, v, scale, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), "pingpong differs from flash_attn_fwd"
+        G.compare_heads(t, {"o": o, "lse": lse}, scale, causal, heads=[(0, 0), (1, 1)], backward=False)
+
+
+def test_pingpong_long_sampled(dev):
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    w = workloads.WORKLOADS["long"]
+    t = workloads.random_case(1, 8, w.N, 128, "bf16", seed=2950, with_do=False)
+    q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+    o, lse = fa.fwd_pingpong(q, k, v, w.scale, True)
+    o2, lse2 = fa.fwd(q, k, v, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    rows = G.sample_rows(w.N, 40, seed=2951)
+    G.compare_heads(t, {"o": o, "lse": lse}, w.scale, True, heads=[(0, 0), (0, 7)], backward=False, rows=rows)
+
+
 # ------------------------------------------------------------------------------ split-key forward
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mode", ["dense", "causal", "mask", "causal+mask"])
