@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_mxfp8_quantize_vt.restype = i
     L.flash_attn_mxfp8_vt_cols.argtypes = [i]
     L.flash_attn_mxfp8_vt_cols.restype = ctypes.c_int64
+    L.flash_attn_bwd_onepass_workspace_bytes.argtypes = [i, i, i, i]
+    L.flash_attn_bwd_onepass_workspace_bytes.restype = sz
+    L.flash_attn_bwd_onepass.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp, vp]
+    L.flash_attn_bwd_onepass.restype = i
     L.flash_attn_fwd_pingpong.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_fwd_pingpong.restype = i
     L.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
@@ -255,6 +259,41 @@ def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float | None = None, cau
                                       _ptr(dv), B, H, N, d, scale, int(bool(causal)), _ptr(bm), _stream(stream))
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+def onepass_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().flash_attn_bwd_onepass_workspace_bytes(B, H, N, d))
+
+
+def bwd_onepass(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, block_mask=None, dq=None,
+                dk=None, dv=None, workspace=None, stream=None):
+    """Backward (bf16, d = 128) in one pass over each key block: dK, dV and dQ from one
+    recomputation of S and P, dQ summed with float32 atomics in the workspace (so dQ's rounding
+    order varies run to run).  Returns (dq, dk, dv)."""
+    import torch
+
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, torch.bfloat16, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with _on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        if workspace is None:
+            need = onepass_workspace_bytes(B, H, N, d)
+            if need == 0:
+                raise FlashAttnError(FA_ERR_UNSUPPORTED, "bwd_onepass")
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    bm = _mask_arg(block_mask, N, dev)
+    st = lib().flash_attn_bwd_onepass(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(workspace), _ws_bytes(workspace), B, H, N, d, scale,
+                                      int(bool(causal)), _ptr(bm), _stream(stream))
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_onepass")
     return dq, dk, dv
 
 

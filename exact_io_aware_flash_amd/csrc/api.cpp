@@ -398,6 +398,36 @@ int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const vo
   return status_of(fa::launch_bwd_bf16(a, stream));
 }
 
+size_t flash_attn_bwd_onepass_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d != 128) return 0;
+  return fa::ws_bytes((long long)B * H, N) + fa::dq_acc_bytes((long long)B * H, N, d);
+}
+
+int flash_attn_bwd_onepass(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes_,
+                           int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask,
+                           hipStream_t stream) {
+  long long elems = 0;
+  int st = bwd_checked(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                       static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse,
+                       static_cast<__bf16*>(dq), static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), workspace,
+                       workspace_bytes_, B, H, N, d, scale, causal, block_mask, true, &elems);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t need = flash_attn_bwd_onepass_workspace_bytes(B, H, N, d);
+  if (workspace_bytes_ < need) return FA_ERR_WORKSPACE;
+  const long long tb = elems * 2, lb = (long long)B * H * N * 4;
+  const long long nb = (N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+  Range in[7] = {rng(q, tb),    rng(k, tb),   rng(v, tb), rng(o, tb), rng(dout, tb), rng(lse, lb),
+                 rng(block_mask, block_mask ? nb * nb : 0)};
+  Range out[4] = {rng(dq, tb), rng(dk, tb), rng(dv, tb), rng(workspace, (long long)need)};
+  st = check_alias(in, 7, out, 4);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = stage_args(q, k, v, o, dout, lse, workspace, dq, dk, dv, B, H, N, d, scale, causal, block_mask);
+  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::ws_bytes((long long)B * H, N));
+  return status_of(fa::launch_bwd_onepass_bf16(a, dq_acc, stream));
+}
+
 int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
                        const float* lse, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes_,
                        int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask,

@@ -974,6 +974,399 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
   }
 }
 
+// ------------------------------------------------------------------ dK, dV and dQ in one pass
+// The pre-pass of the one-pass backward: D per row (as bwd_delta_kernel) and zeros in the row's
+// float32 dQ accumulator, which the one-pass kernel then adds into with atomics.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_zero_kernel(const __bf16* __restrict__ o,
+                                                             const __bf16* __restrict__ dout, float* __restrict__ delta,
+                                                             float* __restrict__ dq_acc, long rows) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 ov = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dout + row * D + part * 8);
+    const __bf16* op = reinterpret_cast<const __bf16*>(&ov);
+    const __bf16* dp = reinterpret_cast<const __bf16*>(&dv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)op[e] * (float)dp[e];
+    f32x4* z = reinterpret_cast<f32x4*>(dq_acc + row * D + part * 8);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    z[0] = zero;
+    z[1] = zero;
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// dQ = scale * (float32 accumulator), rounded to bf16 (8 elements per thread)
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ dq_acc, __bf16* __restrict__ dq,
+                                                             float scale, long n8) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = reinterpret_cast<const f32x4*>(dq_acc)[2 * i];
+  const f32x4 b = reinterpret_cast<const f32x4*>(dq_acc)[2 * i + 1];
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)(a[e] * scale);
+    r[4 + e] = (__bf16)(b[e] * scale);
+  }
+  reinterpret_cast<bf16x8*>(dq)[i] = r;
+}
+
+// One pass over the query tiles of a 128-key block computing dV, dK and the block's share of dQ
+// (d = 128).  Four waves, one per SIMD (512 registers each): wave w owns keys k0 + 32 w .. + 31
+// and, for dQ, features 32 w .. + 31.  Per 32-query part of a query tile:
+//   S = Q K^T, dP = dO V^T         (K, V rows of the wave's keys in registers, Q / dO rows from LDS)
+//   P = exp(S - LSE), dS = P (dP - D)
+//   dV += P^T dO, dK += dS^T Q
+//   dS (bf16) to LDS; after the part barrier every wave reads the dS of all 128 keys (transposed)
+//   and computes dQ[part, its 32 features] = dS K over the block, K^T read transposed from the
+//   block's K rows kept in LDS, then adds it with float32 atomics into the caller's accumulator.
+// Each dQ element gets one atomic add per key block, so the atomics move exactly the bytes of the
+// dQ partials.  The dQ of a part runs in the step of the next part, and its MFMAs carry that part's
+// exponentials in their slots (the dV MFMAs carry dS), so one part's S and dP are live at a time.
+// Query tiles are 64 rows (two parts), double-buffered: with the K block (32 KB) and the dS
+// exchange (16 KB) LDS holds 114 KB.  S, P, dP and dS are the values bwd_dkdv_wave_kernel computes.
+template <bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, Sched sc, float* __restrict__ dq_acc) {
+  constexpr int D = 128, BKV = 128, BQ = 64;
+  constexpr int NH = BQ / 32;
+  constexpr int DC = D / 16, DB = D / 32;
+  using QT = DmaTile<BQ, D>;   // Q or dO rows of a query tile
+  using KB = DmaTile<BKV, D>;  // the key block's K rows
+
+  __shared__ __attribute__((aligned(1024))) char qbuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char obuf1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kblk[KB::BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsbuf[2][4][2048];  // dS of a part: [parity][key group][key][query]
+  __shared__ __attribute__((aligned(16))) float lbuf[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dbuf[2][BQ];
+  __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int bcount;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5,
+            c32 = lane & 31;
+  const int N = a.N;
+  int bh, kt;
+  sched_decode(sc, gridDim.x, bh, kt);
+  const int k0 = kt * BKV;
+  const int k0w = k0 + 32 * w;
+  const size_t base = (size_t)bh * N * D;
+  const size_t rbase = (size_t)bh * N;
+  const __bf16* __restrict__ Qh = a.q + base;
+  const __bf16* __restrict__ Oh = a.dout + base;
+
+  // ---- query tiles (64 rows, two per 128-row mask block) that see this key block
+  const int nqt = (N + BQ - 1) / BQ;
+  int q_first = 0, ntiles = nqt;
+  if (CAUSAL) {
+    q_first = k0 / BQ;
+    ntiles = nqt - q_first;
+  }
+  if (SPARSE) {
+    if (w == 0) {
+      const int cnt = build_block_list(a.mask, a.nb, kt, true, CAUSAL ? kt : 0, a.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = bcount;
+    ntiles = 2 * cnt;
+    if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BQ >= N) ntiles -= 1;  // last block's second half past N
+  }
+  auto tile_start = [&](int t) -> int {
+    if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BQ;
+    return (q_first + t) * BQ;
+  };
+
+  // ---- this lane's key: K (sign of scale folded in) and V rows as the B operands of S and dP
+  const int key = k0w + c32;
+  bf16x8 kreg[DC], vreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    if (key < N) {
+      kreg[c] = xor_sign(*reinterpret_cast<const bf16x8*>(a.k + base + (size_t)key * D + 16 * c + 8 * h), a.ssign);
+      vreg[c] = *reinterpret_cast<const bf16x8*>(a.v + base + (size_t)key * D + 16 * c + 8 * h);
+    } else {
+      kreg[c] = zero_bf16x8();
+      vreg[c] = zero_bf16x8();
+    }
+  }
+  f32x16 dvacc[DB], dkacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dvacc[i] = zero16();
+    dkacc[i] = zero16();
+  }
+  const float sl = a.scale_log2;
+
+  int raddr[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) raddr[c] = QT::off(perm32(c32), 16 * c + 8 * h);
+  int taddr[2][DB];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) taddr[u][db] = QT::off4(8 * h + 4 * u + (j >> 2), 32 * db + 16 * g + 4 * (j & 3));
+  }
+  // transposed read u of a 16-key chunk of dS (rows = keys, 32 queries per 64-byte row): lane j
+  // of its 16-lane group addresses key row 8h + 4u + j/4 (+ 16 (chunk % 2)), queries 16g + 4(j % 4);
+  // and of K^T: key row 8h + 4u + j/4 (+ 16 chunk), features 32 w + 16g + 4(j % 4)
+  int daddr[2], kaddr[2];
+  {
+    const int g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      daddr[u] = (8 * h + 4 * u + (j >> 2)) * 64 + (16 * g + 4 * (j & 3)) * 2;
+      kaddr[u] = KB::off4(8 * h + 4 * u + (j >> 2), 32 * w + 16 * g + 4 * (j & 3));
+    }
+  }
+
+  QT qdma, odma;
+  qdma.init(w, lane);
+  odma.init(w, lane);
+  float lpre = 0.f, dlpre = 0.f;
+  auto rowstats_load = [&](int q0) {
+    if (tid < BQ) {
+      const int qr = q0 + tid;
+      const float l = qr < N ? a.lse[rbase + qr] : neg_inf();
+      lpre = (l == neg_inf()) ? __builtin_huge_valf() : l * kLog2e;
+      dlpre = qr < N ? a.delta[rbase + qr] : 0.f;
+    }
+  };
+  auto rowstats_store = [&](int buf) {
+    if (tid < BQ) {
+      lbuf[buf][tid] = lpre;
+      dbuf[buf][tid] = dlpre;
+    }
+  };
+
+  {
+    KB kdma;
+    kdma.init(w, lane);
+    kdma.issue(a.k + base, N, kblk, k0, w);
+  }
+  if (ntiles > 0) {
+    const int q0 = tile_start(0);
+    qdma.issue(Qh, N, qbuf0, q0, w);
+    odma.issue(Oh, N, obuf0, q0, w);
+    rowstats_load(q0);
+    wait_dma();
+    rowstats_store(0);
+  }
+  wait_dma();
+  __syncthreads();
+
+  // S = Q K^T and dP = dO V^T of part s: register r of half h holds query 32 s + acc_row(r, h) of
+  // the tile, key `key`; operand reads two MFMA pairs ahead; S starts at -inf on masked pairs
+  // (the key tail, and the causal diagonal for the part's queries qs ..).  Compiler MFMAs: the
+  // compiler places the accumulators and inserts the wait states around them.
+  auto sp_chain = [&](const char* tq, const char* to, int s, f32x16& sacc, f32x16& pacc, bool mask, int qs)
+      __attribute__((always_inline)) {
+    bf16x8 qa[DC], oa[DC];
+    auto rd = [&](int c) {
+      qa[c] = lds_b128(tq + raddr[c] + 32 * s * D * 2);
+      oa[c] = lds_b128(to + raddr[c] + 32 * s * D * 2);
+    };
+    rd(0);
+    rd(1);
+    if (mask) {
+      const int thr = key >= N ? 32 : (CAUSAL ? key - qs - 8 * h : 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 16 * (r >> 3) + (r & 7) < thr ? neg_inf() : 0.f;
+    } else {
+      sacc = zero16();
+    }
+    pacc = zero16();
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      if (c + 2 < DC) rd(c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      sacc = mfma32(qa[c], kreg[c], sacc);
+      pacc = mfma32(oa[c], vreg[c], pacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto stat4 = [&](const float* rows, int s, int qq) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(rows + 32 * s + 16 * (qq >> 1) + 8 * h + 4 * (qq & 1));
+  };
+  auto p_quarter = [&](f32x16& x, const f32x4& l, int qq, bf16x8(&pp)[2]) __attribute__((always_inline)) {
+    const int mm = qq >> 1, e0 = 4 * (qq & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * mm + e0 + e;
+      const float p = fast_exp2(__builtin_fmaf(x[r], sl, -l[e]));
+      x[r] = p;
+      pp[mm][e0 + e] = (__bf16)p;
+    }
+  };
+  auto ds_quarter = [&](const f32x16& x, const f32x16& y, const f32x4& d, int qq, bf16x8(&dsp)[2])
+      __attribute__((always_inline)) {
+    const int mm = qq >> 1, e0 = 4 * (qq & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * mm + e0 + e;
+      dsp[mm][e0 + e] = (__bf16)(x[r] * (y[r] - d[e]));
+    }
+  };
+  auto acc_mfma = [](f32x16& acc, const bf16x8& x, const bf16x8& y) __attribute__((always_inline)) {
+    acc = mfma32(x, y, acc);
+  };
+  auto dvdk = [&](const char* tq, const char* to, int s, const bf16x8(&pp)[2], const f32x16& x, const f32x16& y,
+                  const float* Ds, bf16x8(&dsp)[2]) __attribute__((always_inline)) {
+    bf16x8 ob[2 * DB], qb[2 * DB];
+    auto trd = [&](const char* t, int i) -> bf16x8 {
+      const int db = i >> 1, roff = (32 * s + 16 * (i & 1)) * D * 2;
+      return join8(lds_tr4(t + roff + taddr[0][db]), lds_tr4(t + roff + taddr[1][db]));
+    };
+    ob[0] = trd(to, 0);
+    ob[1] = trd(to, 1);
+    f32x4 d = stat4(Ds, s, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      if (i + 2 < 2 * DB) ob[i + 2] = trd(to, i + 2);
+      else qb[i + 2 - 2 * DB] = trd(tq, i + 2 - 2 * DB);
+      acc_mfma(dvacc[i >> 1], pp[i & 1], ob[i]);
+      if (i & 1) {
+        const int qq = i >> 1;
+        const f32x4 dc = d;
+        if (qq + 1 < 4) d = stat4(Ds, s, qq + 1);
+        ds_quarter(x, y, dc, qq, dsp);
+        if (qq & 1) asm volatile("" : "+v"(dsp[qq >> 1]));  // computed in this slot
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      if (i + 2 < 2 * DB) qb[i + 2] = trd(tq, i + 2);
+      acc_mfma(dkacc[i >> 1], dsp[i & 1], qb[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // dQ of the part whose dS is in dsbuf[par] (queries qs ..): 8 MFMAs over the block's 128 keys
+  // (dS and K^T read transposed), then 16 float32 atomic adds of the wave's 32 features: register
+  // r of half h holds query qs + 8 (r / 4) + 4h + r % 4, feature 32 w + c32.  The adds go through a
+  // buffer resource that starts at row qs and ends at row N: the per-lane offsets are fixed (rows
+  // 8 (r / 4) + 4h, the r % 4 part in the instruction's offset), and the hardware range check drops
+  // the adds of rows past N.  Every add is issued, so the count per step is fixed.
+  int avo[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) avo[m] = ((8 * m + 4 * h) * D + 32 * w + c32) * 4;
+  auto dq_part = [&](int par, int qs, auto hook) __attribute__((always_inline)) {
+    f32x16 acc;
+    bf16x8 dsa[8], kta[8];
+    auto rd = [&](int j) {
+      const char* src = &dsbuf[par][j >> 1][0] + 16 * (j & 1) * 64;
+      dsa[j] = join8(lds_tr4(src + daddr[0]), lds_tr4(src + daddr[1]));
+      const char* ksrc = kblk + 16 * j * D * 2;
+      kta[j] = join8(lds_tr4(ksrc + kaddr[0]), lds_tr4(ksrc + kaddr[1]));
+    };
+    rd(0);
+    rd(1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 2 < 8) rd(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      acc = mfma32(dsa[j], kta[j], j == 0 ? zero16() : acc);
+      hook(j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const Rsrc rs = make_rsrc(dq_acc + (rbase + qs) * D, max(N - qs, 0) * D * 4);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rs, avo[r >> 2] + (r & 3) * D * 4, 0, 0);
+  };
+
+  auto step = [&](int t, auto parity) {
+    constexpr int par = decltype(parity)::value;
+    const char* tq = par ? qbuf1 : qbuf0;
+    const char* to = par ? obuf1 : obuf0;
+    const int q0 = tile_start(t);
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) {
+      const int qn = tile_start(t + 1);
+      qdma.issue(Qh, N, par ? qbuf0 : qbuf1, qn, w);
+      odma.issue(Oh, N, par ? obuf0 : obuf1, qn, w);
+      rowstats_load(qn);
+    }
+    const float* Ls = lbuf[par];
+    const float* Ds = dbuf[par];
+    auto part_mask = [&](int qs) -> bool { return (k0w + 32 > N) || (CAUSAL && qs < k0w + 31); };
+    // Part s of the tile: the S / dP MFMAs; then the previous part's dQ MFMAs with this part's
+    // exponentials in their slots (a quarter of P per two MFMAs, the LSE read one quarter ahead)
+    // and its atomic adds; then dV (dS in its slots) and dK; dS to LDS; the part barrier.
+#pragma unroll
+    for (int s = 0; s < NH; ++s) {
+      const int qs = q0 + 32 * s;
+      f32x16 x, y;  // S (then P in fp32) and dP of the part
+      bf16x8 pp[2], dsp[2];
+      sp_chain(tq, to, s, x, y, part_mask(qs), qs);
+      f32x4 l = stat4(Ls, s, 0);
+      auto quarter = [&](int qq) __attribute__((always_inline)) {
+        const f32x4 lc = l;
+        if (qq + 1 < 4) l = stat4(Ls, s, qq + 1);
+        p_quarter(x, lc, qq, pp);
+        if (qq & 1) asm volatile("" : "+v"(pp[qq >> 1]));  // computed in this slot
+      };
+      auto quarter_slot = [&](int j) __attribute__((always_inline)) {
+        if (j & 1) quarter(j >> 1);
+      };
+      if (s > 0)
+        dq_part(0, q0, quarter_slot);
+      else if (t > 0)
+        dq_part(1, tile_start(t - 1) + 32, quarter_slot);
+      else {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) quarter(qq);
+      }
+      dvdk(tq, to, s, pp, x, y, Ds, dsp);
+      // dS of this part (global part 2t + s, parity s) to LDS: key c32 of the group, queries
+      // 16 mm + 8h ..
+      char* dsw = &dsbuf[s][w][0] + c32 * 64 + 16 * h;
+      *reinterpret_cast<bf16x8*>(dsw) = dsp[0];
+      *reinterpret_cast<bf16x8*>(dsw + 32) = dsp[1];
+      if (s == NH - 1) {
+        if (has_next) rowstats_store(par ^ 1);
+        // the next tile's copies were issued before this tile's atomic adds (16 per dQ part)
+        if (t > 0)
+          wait_vm<32>();
+        else
+          wait_vm<16>();
+      }
+      lds_barrier();
+    }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (ntiles > 0) dq_part(1, tile_start(ntiles - 1) + 32, [](int) {});  // the last part's dQ
+
+  // ---- epilogue: lane holds feature 32 db + c32 of keys k0w + 8 g + 4 h + e (register 4 g + e)
+  const float scale = a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = k0w + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (kr < N) {
+        const size_t off = base + (size_t)kr * D + 32 * db + c32;
+        a.dv[off] = (__bf16)dvacc[db][r];
+        a.dk[off] = (__bf16)(dkacc[db][r] * scale);
+      }
+    }
+}
+
 template <int D>
 hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
   const long rows = (long)a.BH * a.N;
@@ -1028,7 +1421,45 @@ struct DqL {
   static hipError_t run(const BwdArgs& a, hipStream_t st) { return launch_dq_t<D, C, S>(a, st); }
 };
 
+template <bool C, bool S>
+hipError_t launch_fused_t(const BwdArgs& a, float* dq_acc, hipStream_t st) {
+  const int nkv = (a.N + 127) / 128;
+  static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_fused_kernel<C, S>), 256);
+  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+  hipLaunchKernelGGL((bwd_fused_kernel<C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc, dq_acc);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_prepass_zero_bf16(const BwdArgs& a, float* dq_acc, hipStream_t st) {
+  const long rows = (long)a.BH * a.N;
+  constexpr int RPB = 256 / (128 / 8);
+  hipLaunchKernelGGL((bwd_delta_zero_kernel<128>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o,
+                     a.dout, a.delta, dq_acc, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdvq_bf16(const BwdArgs& a, float* dq_acc, hipStream_t st) {
+  const bool c = a.causal != 0, s = a.mask != nullptr;
+  if (c) return s ? launch_fused_t<true, true>(a, dq_acc, st) : launch_fused_t<true, false>(a, dq_acc, st);
+  return s ? launch_fused_t<false, true>(a, dq_acc, st) : launch_fused_t<false, false>(a, dq_acc, st);
+}
+
+hipError_t launch_bwd_dq_convert_bf16(const BwdArgs& a, const float* dq_acc, hipStream_t st) {
+  const long n8 = (long)a.BH * a.N * a.d / 8;
+  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dq_acc, a.dq, a.scale,
+                     n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_onepass_bf16(const BwdArgs& a, float* dq_acc, hipStream_t stream) {
+  hipError_t e = launch_bwd_prepass_zero_bf16(a, dq_acc, stream);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdvq_bf16(a, dq_acc, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_convert_bf16(a, dq_acc, stream);
+}
 
 hipError_t launch_bwd_delta_bf16(const BwdArgs& a, hipStream_t stream) {
   return a.d == 64 ? launch_delta_t<64>(a, stream) : launch_delta_t<128>(a, stream);

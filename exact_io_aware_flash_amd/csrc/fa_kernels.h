@@ -153,6 +153,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_delta_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
+// one-pass backward (d = 128): the pre-pass also zeroes the float32 dQ accumulator [BH, N, d],
+// one kernel computes dK, dV and adds dQ with atomics, a last one converts dQ to bf16 (x scale)
+inline size_t dq_acc_bytes(long long BH, int N, int d) { return (size_t)BH * N * d * 4; }
+hipError_t launch_bwd_onepass_bf16(const BwdArgs& a, float* dq_acc, hipStream_t stream);
+hipError_t launch_bwd_prepass_zero_bf16(const BwdArgs& a, float* dq_acc, hipStream_t stream);
+hipError_t launch_bwd_dkdvq_bf16(const BwdArgs& a, float* dq_acc, hipStream_t stream);
+hipError_t launch_bwd_dq_convert_bf16(const BwdArgs& a, const float* dq_acc, hipStream_t stream);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
 

@@ -209,6 +209,24 @@ int flash_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                    int B, int H, int N, int d, float scale, int causal,
                    const uint8_t *block_mask, hipStream_t stream);
 
+/* Backward, bf16, d = 128, in one pass over each key block ([P3 "Innovation #3"]): one
+ * recomputation of S and P per (key block, query tile) yields dV, dK and the block's share of dQ,
+ * which is added with float32 atomics into an accumulator in the workspace (zeroed by the
+ * pre-pass kernel, converted to bf16 times scale at the end).  Same definition, arguments and
+ * checks as flash_attn_bwd; dV equals flash_attn_bwd's bit for bit, dK and dQ agree with it up to
+ * rounding (dS formed from P in float32; dQ's float32 sums in an order that varies run to run).
+ *   workspace   at least flash_attn_bwd_onepass_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *               aligned: D (float32 [B, H, N], rounded up to 256 bytes), then the dQ accumulator
+ *               (float32 [B, H, N, d]); contents undefined afterwards.
+ *   d != 128 gives FA_ERR_UNSUPPORTED. */
+size_t flash_attn_bwd_onepass_workspace_bytes(int B, int H, int N, int d);
+int flash_attn_bwd_onepass(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse,
+                           void *dq, void *dk, void *dv,
+                           void *workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t *block_mask, hipStream_t stream);
+
 /* Backward with float32 tensors and arithmetic; same definition and arguments. */
 int flash_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                        const float *dout, const float *lse,
@@ -258,7 +276,9 @@ int flash_attn_bwd_dq(const void *q, const void *k, const void *v, const void *d
  *   (on different streams, or from different host threads without ordering) race on it and give
  *   undefined results.  Calls ordered on one stream are safe; every row of D is rewritten by
  *   each call before it is read, so nothing carries over from the previous call.
- *   FA_ERR_HIP also reports a failed lookup of the array's device address. */
+ *   FA_ERR_HIP also reports a failed lookup of the array's device address.  That lookup
+ *   (hipGetSymbolAddress) runs on the first call on each device: make that first call outside
+ *   stream capture; later calls make no HIP call but the kernel launches. */
 #define FA_NOALLOC_MAX_ROWS 4194304
 int flash_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
                            const void *dout, const float *lse,

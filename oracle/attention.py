@@ -149,10 +149,11 @@ def backward_head(q, k, v, do, scale, causal=False, block_mask=None, dq_rows=Non
     want_row[dq_rows] = True
     row_pos = np.full(N, -1, dtype=np.int64)
     row_pos[dq_rows] = np.arange(dq_rows.size)
-    for a in range(0, N, chunk):
-        r = np.arange(a, min(N, a + chunk))
-        if dkv_cols.size == 0 and not want_row[r].any():
-            continue
+    # dK and dV sum over every query row; dQ of a row needs only that row's P, dP and D, so
+    # without dK/dV columns only the requested rows are visited
+    visit = np.arange(N) if dkv_cols.size else np.unique(dq_rows)
+    for a in range(0, visit.size, chunk):
+        r = visit[a:a + chunk]
         P, _, _ = _softmax_rows(_scores(q, k, r, scale, causal, block_mask))
         dP = do[r] @ v.T
         D = (P * dP).sum(axis=1)

@@ -140,3 +140,42 @@ def sample_rows(N, n, seed):
     base = {0, 1, N - 1, N // 2, min(N - 1, 127), min(N - 1, 128)}
     base |= set(rng.choice(N, size=min(N, n), replace=False).tolist())
     return np.array(sorted(base))
+
+
+def tile_samples(N, seed, tile=128):
+    """One seeded random index in every `tile`-sized block of [0, N) (the ragged last block too)."""
+    rng = np.random.default_rng(seed)
+    nt = (N + tile - 1) // tile
+    return np.minimum(np.arange(nt) * tile + rng.integers(0, tile, nt), N - 1)
+
+
+def compare_every_tile(t: workloads.Tensors, res, scale, causal, seed, kv_heads, backward=True):
+    """Full-size comparison that reaches every tile: on every head, one query row of every
+    128-row query tile (O, LSE and, with the backward, dQ); on the heads `kv_heads`, one key of
+    every 128-key block (dK, dV).  Rows and keys are drawn per head."""
+    import oracle
+
+    B, H, N = t.q.shape[:3]
+    bf16 = t.dtype == "bf16"
+    tol = TOL_BF16 if bf16 else TOL_F32
+    worst = {"O": 0.0, "LSE": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    for b in range(B):
+        for h in range(H):
+            q, k, v = _head(t, "q", b, h), _head(t, "k", b, h), _head(t, "v", b, h)
+            r = tile_samples(N, seed + 1000 * b + h)
+            O, L = oracle.forward_head(q, k, v, scale, causal, t.block_mask, rows=r)
+            worst["O"] = max(worst["O"], check(f"O[{b},{h}] tiles", host_f64(res["o"][b, h][r]), O, tol, bf16))
+            worst["LSE"] = max(worst["LSE"], check_lse(f"LSE[{b},{h}] tiles", res["lse"][b, h][r].cpu().numpy(), L))
+            if backward:
+                do = _head(t, "do", b, h)
+                dQ, _, _ = oracle.backward_head(q, k, v, do, scale, causal, t.block_mask, dq_rows=r, dkv_cols=[])
+                worst["dQ"] = max(worst["dQ"], check(f"dQ[{b},{h}] tiles", host_f64(res["dq"][b, h][r]), dQ, tol, bf16))
+                if (b, h) in kv_heads:
+                    c = tile_samples(N, seed + 7 + 1000 * b + h)
+                    _, dK, dV = oracle.backward_head(q, k, v, do, scale, causal, t.block_mask, dq_rows=[], dkv_cols=c)
+                    worst["dK"] = max(worst["dK"], check(f"dK[{b},{h}] blocks", host_f64(res["dk"][b, h][c]), dK, tol,
+                                                         bf16))
+                    worst["dV"] = max(worst["dV"], check(f"dV[{b},{h}] blocks", host_f64(res["dv"][b, h][c]), dV, tol,
+                                                         bf16))
+    say(f"  worst over all tiles: {worst}")
+    return worst

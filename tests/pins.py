@@ -282,3 +282,7 @@ def check_sampled_backward(backward_head, seed=13):
     sq, sk, sv = backward_head(q, k, v, do, 0.5, True, mask, dq_rows=rows, dkv_cols=cols, chunk=37)
     assert np.abs(sq - dQ[rows]).max() <= 1e-12 and np.abs(sk - dK[cols]).max() <= 1e-12
     assert np.abs(sv - dV[cols]).max() <= 1e-12, "sampled backward equals full"
+    # dQ rows alone (no dK/dV columns: only the requested rows are visited), unsorted
+    sel = [299, 5, 200, 99, 130]
+    sq2, sk2, sv2 = backward_head(q, k, v, do, 0.5, True, mask, dq_rows=np.array(sel), dkv_cols=[], chunk=2)
+    assert np.abs(sq2 - dQ[sel]).max() <= 1e-12 and sk2.shape == (0, 4) and sv2.shape == (0, 4)

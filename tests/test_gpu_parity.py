@@ -46,25 +46,37 @@ def test_bert_shaped_full(dev):
     _run_and_compare("bert", t, w.scale, w.causal, dev, heads)
 
 
+def _run_every_tile(name, w, t, dev, seed, kv_heads, backward=True):
+    G.say(f"[case] {name}: shape={t.q.shape} causal={w.causal} mask={'yes' if t.block_mask is not None else 'no'} "
+          f"bwd={backward} (one row per query tile on every head; one key per key block on {len(kv_heads)} heads)")
+    t0 = time.time()
+    res = G.run_lib(t, w.scale, w.causal, dev, backward)
+    G.say(f"  device done in {time.time() - t0:.1f}s")
+    G.compare_every_tile(t, res, w.scale, w.causal, seed, kv_heads, backward)
+
+
+def _spread_heads(B, H, n):
+    """n heads spread over the (b, h) grid, first and last included."""
+    idx = np.unique(np.linspace(0, B * H - 1, n).round().astype(int))
+    return {(int(i) // H, int(i) % H) for i in idx}
+
+
 def test_gpt2_shaped_causal(dev):
     w = workloads.WORKLOADS["gpt2"]
     t = workloads.make(w)
-    _run_and_compare("gpt2", t, w.scale, w.causal, dev, heads=[(0, 0), (3, 7), (7, 11)])
+    _run_every_tile("gpt2", w, t, dev, seed=30, kv_heads=_spread_heads(w.B, w.H, 8))
 
 
-def test_long_context_causal_sampled(dev):
+def test_long_context_causal_every_tile(dev):
     w = workloads.WORKLOADS["long"]
     t = workloads.make(w)
-    rows = G.sample_rows(w.N, 48, seed=7)
-    cols = G.sample_rows(w.N, 24, seed=8)
-    _run_and_compare("long", t, w.scale, w.causal, dev, heads=[(0, 0), (0, 31)], rows=rows, cols=cols)
+    _run_every_tile("long", w, t, dev, seed=40, kv_heads=_spread_heads(w.B, w.H, 8))
 
 
-def test_long_context_64k_forward_sampled(dev):
+def test_long_context_64k_forward_every_tile(dev):
     w = workloads.WORKLOADS["long64k"]
     t = workloads.make(w, with_do=False)
-    rows = G.sample_rows(w.N, 48, seed=9)
-    _run_and_compare("long64k fwd", t, w.scale, w.causal, dev, heads=[(0, 0), (0, 7)], backward=False, rows=rows)
+    _run_every_tile("long64k fwd", w, t, dev, seed=50, kv_heads=set(), backward=False)
 
 
 def test_head_major_schedule_sampled(dev):
@@ -80,7 +92,7 @@ def test_head_major_schedule_sampled(dev):
 def test_block_sparse(dev):
     w = workloads.WORKLOADS["sparse"]
     t = workloads.make(w)
-    _run_and_compare("sparse", t, w.scale, w.causal, dev, heads=[(0, 0), (3, 15)])
+    _run_every_tile("sparse", w, t, dev, seed=60, kv_heads=_spread_heads(w.B, w.H, 8))
 
 
 # ------------------------------------------------------------------------------ sweeps and edges
@@ -255,6 +267,47 @@ def test_explicit_stream_argument(dev):
     assert torch.equal(so[0], ref_s[0]) and torch.equal(so[1], ref_s[1])
 
 
+def test_graph_capture_replays(dev):
+    """The library's launches (forward, the three backward stages, the allocation-free backward)
+    captured into one HIP graph: every replay, with eager work and synchronisations between
+    replays, equals the eager results bitwise."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    t = workloads.random_case(2, 4, 777, 128, "bf16", seed=760)
+    q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+    o, lse = fa.fwd(q, k, v, 0.1, True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, 0.1, True)
+    torch.cuda.synchronize()
+    go, gl = torch.empty_like(o), torch.empty_like(lse)
+    gq, gk, gv, nq, nk, nv = (torch.empty_like(q) for _ in range(6))
+    ws = fa.new_workspace(2, 4, 777, 128, dev)
+    # warm: the launchers' one-time queries and the scratch lookup of the allocation-free entry
+    # point run eagerly, outside the capture
+    fa.fwd(q, k, v, 0.1, True, out=go, lse=gl)
+    fa.bwd_noalloc(q, k, v, go, gl, do, nq, nk, nv, 0.1, True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fwd(q, k, v, 0.1, True, out=go, lse=gl)
+        fa.bwd_preprocess(q, go, do, ws)
+        fa.bwd_dkdv(q, k, v, do, gl, ws, 0.1, True, None, gk, gv)
+        fa.bwd_dq(q, k, v, do, gl, ws, 0.1, True, None, gq)
+        fa.bwd_noalloc(q, k, v, go, gl, do, nq, nk, nv, 0.1, True)
+    for r in range(3):
+        for x in (go, gl, gq, gk, gv, nq, nk, nv):
+            x.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(go, o) and torch.equal(gl, lse), f"replay {r}: forward"
+        for a, b in ((gq, dq), (gk, dk), (gv, dv), (nq, dq), (nk, dk), (nv, dv)):
+            assert torch.equal(a, b), f"replay {r}: backward"
+        del junk
+
+
 def test_invalid_call_leaves_outputs_untouched(dev):
     import ctypes
 
@@ -315,6 +368,53 @@ def test_autograd_wrapper(dev):
     assert torch.equal(qa.grad, dq_ref) and torch.equal(ka.grad, dk_ref) and torch.equal(va.grad, dv_ref)
     res = {"o": o.detach(), "lse": lse_ref, "dq": qa.grad, "dk": ka.grad, "dv": va.grad}
     G.compare_heads(t, res, 0.125, True, heads=[(0, 0), (0, 1)])
+
+
+# ------------------------------------------------------------------------------ one-pass backward
+@pytest.mark.parametrize("mode", ["dense", "causal", "mask", "causal+mask"])
+def test_onepass_backward_matches_oracle(dev, mode):
+    """The one-pass backward (dQ by float32 atomics): dV bitwise equal to flash_attn_bwd's, dQ, dK
+    and dV within the bar of the oracle; ragged N from one tile to many, both signs of scale."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    causal = "causal" in mode
+    for N, scale in ((1, 0.09), (65, 0.09), (300, -0.09), (1000, 0.09), (2049, 0.11)):
+        t = workloads.random_case(1, 2, N, 128, "bf16", seed=3300 + N, mask_density=0.6 if "mask" in mode else None,
+                                  mask_seed=3400 + N)
+        if t.block_mask is not None:
+            np.fill_diagonal(t.block_mask, 1)
+        G.say(f"[case] onepass N={N} {mode} scale={scale}")
+        q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+        mask = torch.from_numpy(t.block_mask).to(dev) if t.block_mask is not None else None
+        o, lse = fa.fwd(q, k, v, scale, causal, mask)
+        nan = lambda: torch.full_like(q, float("nan"))
+        dq, dk, dv = fa.bwd_onepass(q, k, v, o, lse, do, scale, causal, mask, dq=nan(), dk=nan(), dv=nan())
+        rq, rk, rv = fa.bwd(q, k, v, o, lse, do, scale, causal, mask)
+        torch.cuda.synchronize()
+        for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert not torch.isnan(x).any().item(), f"{name}: unwritten elements"
+        # dV is the same sum of the same bf16 P in the same order; dK may differ by rounding (the
+        # two-kernel path forms dS from the bf16 P its waves exchange, this kernel from fp32 P)
+        assert torch.equal(dv, rv), "dV differs from flash_attn_bwd"
+        G.compare_heads(t, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, scale, causal, heads=[(0, 0), (0, 1)])
+
+
+def test_onepass_backward_long_every_tile(dev):
+    """The long-context workload through the one-pass backward, every query tile of every head."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    w = workloads.WORKLOADS["long"]
+    t = workloads.make(w)
+    q, k, v, do = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v, t.do))
+    o, lse = fa.fwd(q, k, v, w.scale, True)
+    dq, dk, dv = fa.bwd_onepass(q, k, v, o, lse, do, w.scale, True)
+    torch.cuda.synchronize()
+    res = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    G.compare_every_tile(t, res, w.scale, True, seed=45, kv_heads={(0, 3), (0, 30)})
 
 
 # ------------------------------------------------------------------------------ wave-specialised forward
