@@ -43,13 +43,22 @@ class FlashAttnError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load libflash_attn.so (raises if it is missing: there is no other implementation)."""
+    """Load libflash_attn.so (raises if it is missing: there is no other implementation).  The
+    environment variable FLASH_ATTN_LIB names another build of the same library instead (the
+    checking builds: host sanitizers, LDS sentinels)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m exact_io_aware_flash_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    path = os.environ.get("FLASH_ATTN_LIB") or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with `python -m exact_io_aware_flash_amd.build`")
+    _lib = load(path)
+    return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` and declare its entry points."""
+    L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
     L.flash_attn_fwd.restype = i
@@ -91,7 +100,6 @@ def lib() -> ctypes.CDLL:
     L.flash_attn_bwd_noalloc.restype = i
     L.flash_attn_status_string.argtypes = [i]
     L.flash_attn_status_string.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -686,6 +686,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
         pv[0] = lds_b128(pb + 16 * lane);
         pv[1] = lds_b128(pb + 1024 + 16 * lane);
         dr = stat_load(Ds_d, s_d);
+#ifdef FA_CHECK
+        // checking build: P consumed, its slots read as NaN until the P wave writes the next part
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(pv[0]), "+v"(pv[1]));
+        lds_sentinel(const_cast<char*>(pb), 2, lane);
+#endif
       }
       const f32x16& xd = dpv[s_d & 1];
       auto dslot = [&](int c) __attribute__((always_inline)) {

@@ -135,6 +135,22 @@ __device__ __forceinline__ constexpr int sw_dual(int row) {
   return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
+// Checking build (-DFA_CHECK): before a wave starts an asynchronous copy into LDS it fills the
+// 16-byte chunks the copy will land in with NaN (0xFF bytes: NaN in bf16 and in E4M3), so that a
+// read of the tile that runs ahead of the copy (a missing wait or barrier) carries NaN into the
+// results.  `dst` is the first of `n` 1 KB blocks this wave fills, lane i at offset 16 i.
+__device__ __forceinline__ void lds_sentinel(char* dst, int n, int lane) {
+#ifdef FA_CHECK
+  const uint4 nan4 = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+  for (int i = 0; i < n; ++i) *reinterpret_cast<uint4*>(dst + 1024 * i + 16 * lane) = nan4;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)dst;
+  (void)n;
+  (void)lane;
+#endif
+}
+
 template <int R, int D, int NW = 4>
 struct DmaTile {
   static constexpr int CPR = D / 8;
@@ -159,6 +175,7 @@ struct DmaTile {
   // as zero.  The resource starts at row0 and spans only rows row0 .. N-1, so the hardware
   // range check (which covers the per-lane offset) does the clipping.
   __device__ __forceinline__ void issue(const __bf16* head, int N, char* tile, int row0, int w) const {
+    lds_sentinel(tile + 1024 * CH * w, CH, __lane_id());
     const Rsrc r = make_rsrc(head + (size_t)row0 * D, max(N - row0, 0) * D * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) dma16(r, tile + 1024 * (CH * w + i), voff[i], 0);

@@ -293,11 +293,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     vcopy[i] = row * Np + ((pch ^ sw_v8(row)) << 4);
   }
   auto issue_k = [&](char* buf, int k0) {
+    lds_sentinel(buf + 1024 * KI * w, KI, lane);
     const Rsrc r = make_rsrc(K8 + (size_t)k0 * D, max(N - k0, 0) * D);
 #pragma unroll
     for (int i = 0; i < KI; ++i) dma16(r, buf + 1024 * (KI * w + i), kcopy[i], 0);
   };
   auto issue_v = [&](char* buf, int k0) {
+    lds_sentinel(buf + 1024 * VI * w, VI, lane);
     const Rsrc r = make_rsrc(VT8 + k0, D * Np - k0);
 #pragma unroll
     for (int i = 0; i < VI; ++i) dma16(r, buf + 1024 * (VI * w + i), vcopy[i], 0);

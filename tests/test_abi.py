@@ -5,6 +5,7 @@ import ctypes
 import glob
 import os
 import re
+import sys
 
 import pytest
 
@@ -164,6 +165,7 @@ def test_bwd_argument_errors(L, f32):
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     import exact_io_aware_flash_amd as fa
+    monkeypatch.delenv("FLASH_ATTN_LIB", raising=False)
     monkeypatch.setattr(fa, "_lib", None)
     monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
@@ -349,3 +351,26 @@ def test_pingpong_argument_errors(L):
     assert call(d=96) == fa.FA_ERR_HEADDIM
     assert call(scale=0.0) == fa.FA_ERR_SCALE
     assert call(o=q) == fa.FA_ERR_ALIAS
+
+
+def test_validation_under_host_sanitizers():
+    """The argument checks of the C ABI, every case of this file, run against the build whose host
+    code carries AddressSanitizer and UndefinedBehaviorSanitizer (overflowing products, bad shifts,
+    out-of-bounds reads in the validators abort the run with a report)."""
+    import subprocess
+
+    from exact_io_aware_flash_amd import build as B
+    lib = B.variant_path("asan")
+    rt = B.sanitizer_runtime()
+    if not os.path.exists(lib) or rt is None:
+        pytest.skip("sanitized build or sanitizer runtime missing (built by exact_io_aware_flash_amd.build)")
+    syms = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout
+    assert "__asan_report" in syms and "__ubsan_handle" in syms, "the asan build is not instrumented"
+    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", FLASH_ATTN_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.abspath(__file__), "-q", "-p", "no:cacheprovider",
+                        "-k", "not sanitizers"], capture_output=True, text=True, env=env, timeout=600,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    out = r.stdout + r.stderr
+    assert r.returncode == 0, out[-4000:]
+    assert "ERROR: AddressSanitizer" not in out and "runtime error:" not in out, out[-4000:]
