@@ -251,6 +251,8 @@ struct Sched {
   int remap;       // 1: XCD-aware remap active
   int head_major;  // 1: head-major order inside a group (needs remap)
   int heavy_last_tile;  // 1: tile ntiles-1 is the heaviest (query side); 0: tile 0 is
+  int slots;       // workgroups resident per XCD when a kernel alternates its key direction by
+                   // cohort (sched_descending), else 0
 };
 
 __device__ __forceinline__ void sched_decode(const Sched& s, int total, int& bh, int& tile) {
@@ -269,6 +271,23 @@ __device__ __forceinline__ void sched_decode(const Sched& s, int total, int& bh,
   }
   tile = s.heavy_last_tile ? (s.ntiles - 1 - t) : t;
   bh = hg * s.group + hh;
+}
+
+// Key direction of a causal query tile under head-major order.  The XCD's slots fill with the
+// heaviest tiles of a head all at once (a cohort that starts together and, each tile one unit
+// shorter than the last, ends staggered); each freed slot takes the next-heaviest tile, so the
+// following cohort starts staggered and ends together, and so on alternately.  Walking the keys
+// upwards from key 0 in the cohorts that start together and downwards from the diagonal in those
+// that end together keeps the workgroups of a cohort on about the same K/V tile at any moment, so
+// one L2 fill of a tile serves all of them, where the staggered starts of a single direction
+// spread them over the slots' worth of query tiles of K/V (4 MiB at d = 128 with 8192 query rows
+// in flight: an L2's whole size).
+__device__ __forceinline__ bool sched_descending(const Sched& s, int total) {
+  if (!s.slots || !s.head_major) return false;
+  int w = blockIdx.x;
+  if (s.remap) w = (w & 7) * (total >> 3) + (w >> 3);
+  const int r = w % (s.group * s.ntiles);  // position in the XCD's dispatch order
+  return (r / s.slots) & 1;
 }
 
 // Builds, in LDS, the ascending list of mask blocks J with block_mask[I][J] != 0 (row mode) or

@@ -99,10 +99,11 @@ inline int xcd_slots(const void* kernel, int block_threads = 256) {
   return per_cu * (cus / 8);
 }
 
-inline Sched make_sched(int ntiles, int BH, int heavy_last_tile, int slots_per_xcd) {
+inline Sched make_sched(int ntiles, int BH, int heavy_last_tile, int slots_per_xcd, bool alternate = false) {
   Sched s;
   s.ntiles = ntiles;
   s.heavy_last_tile = heavy_last_tile;
+  s.slots = alternate ? slots_per_xcd : 0;
   if (BH % 8 == 0) {
     s.remap = 1;
     s.group = BH / 8;

@@ -93,9 +93,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void fwd_
     ntiles = 2 * cnt;
     if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BC >= N) ntiles -= 1;  // tail block half past N
   }
+  // causal tiles of alternate cohorts walk the keys from the diagonal down (sched_descending);
+  // the masks below depend only on each tile's first key, not on the order
+  const bool desc = CAUSAL && !SPARSE && !SPLIT && sched_descending(sc, gridDim.x);
   auto tile_start = [&](int t) -> int {
     if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
-    return (tlo + t) * BC;
+    return (desc ? tend - 1 - t : tlo + t) * BC;
   };
 
   // ---- Q^T operand in registers (B operand: lane holds query q0 + 32w + c32, features 16c + 8h ..)
@@ -407,6 +410,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched s
   const __bf16* __restrict__ V = a.v + base;
   int T = (N + BC - 1) / BC;
   if (CAUSAL) T = min(T, (min(q0 + BR, N) - 1) / BC + 1);
+  // first key of the j-th tile visited: causal tiles of alternate cohorts walk the keys
+  // downwards from the diagonal (sched_descending), as in fwd_bf16_kernel
+  const bool desc = CAUSAL && sched_descending(sc, gridDim.x);
+  auto kstart = [&](int j) -> int { return (desc ? T - 1 - j : j) * BC; };
 
   const int qrow = q0 + 32 * w + c32;
   bf16x8 qreg[DC];
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched s
   // fwd_bf16_kernel), rescale of O, P = exp2(S scale log2(e) - m) in fp32 for the row sums and
   // as bf16 for PV
   auto vphase = [&](int j) __attribute__((always_inline)) {
-    const int k0 = j * BC;
+    const int k0 = kstart(j);
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0 + 32 * w)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -519,11 +526,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched s
     constexpr int r = decltype(rc)::value;  // i % 3
     int n = 0;
     if (i < T) {
-      kdma.issue(K, N, kbuf[r], i * BC, w);
+      kdma.issue(K, N, kbuf[r], kstart(i), w);
       n += KT::CH;
     }
     if (i - 1 < T) {
-      vdma.issue(V, N, vbuf[(r + 2) % 3], (i - 1) * BC, w);
+      vdma.issue(V, N, vbuf[(r + 2) % 3], kstart(i - 1), w);
       n += KT::CH;
     }
     return n;
@@ -559,9 +566,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched s
 
   // prologue: K[0], K[1], V[0] by every wave, and group 1's share of K[2], V[1] (group 0 copies
   // its share at the start of M_0); then group 1's idle phase
-  kdma.issue(K, N, kbuf[0], 0, w);
-  if (T > 1) kdma.issue(K, N, kbuf[1], BC, w);
-  vdma.issue(V, N, vbuf[0], 0, w);
+  kdma.issue(K, N, kbuf[0], kstart(0), w);
+  if (T > 1) kdma.issue(K, N, kbuf[1], kstart(1), w);
+  vdma.issue(V, N, vbuf[0], kstart(0), w);
   wait_vm<0>();
   lds_barrier();
   if (grp != 0) {
@@ -657,7 +664,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int BR = 32 * NW;
   const int nq = (a.N + BR - 1) / BR;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S, false, NW>), 64 * NW);
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C && !S);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S, false, NW>), dim3(nq * a.BH), dim3(64 * NW), 0, st, a, sc);
   return hipGetLastError();
 }
@@ -666,7 +673,7 @@ template <bool C>
 static hipError_t launch_pingpong_t(const FwdArgs& a, hipStream_t st) {
   const int nq = (a.N + 255) / 256;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_pingpong_kernel<C>), 512);
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C);
   hipLaunchKernelGGL((fwd_pingpong_kernel<C>), dim3(nq * a.BH), dim3(512), 0, st, a, sc);
   return hipGetLastError();
 }

@@ -223,9 +223,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     ntiles = 2 * cnt;
     if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BC >= N) ntiles -= 1;  // tail block half past N
   }
+  // causal tiles of alternate cohorts walk the keys downwards from the diagonal (sched_descending);
+  // the masks depend only on each tile's first key
+  const bool desc = CAUSAL && !SPARSE && sched_descending(sc, gridDim.x);
   auto tile_start = [&](int t) -> int {
     if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
-    return t * BC;
+    return (desc ? ntiles - 1 - t : t) * BC;
   };
 
   // ---- Q operand (B): lane holds query q0 + 32 w + c32, features 64 f + 16 h .. and 64 f + 32 + 16 h ..
@@ -526,7 +529,7 @@ static hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t st) {
   constexpr int BR = 128;
   const int nq = (a.N + BR - 1) / BR;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_mxfp8_kernel<D, C, S>));
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C && !S);
   hipLaunchKernelGGL((fwd_mxfp8_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
