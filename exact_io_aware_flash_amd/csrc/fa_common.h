@@ -232,6 +232,21 @@ __device__ __forceinline__ float row_bcast(float v, int k) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Q^T operand of one lane held in registers: features 16 c + 8 h .. 16 c + 8 h + 7 of query row
+// qrow for every 16-wide chunk c, the sign of the scale folded in (xor_sign).  Rows past N load
+// row N - 1 and are zeroed after, so the loads have no branch around them and are all in flight
+// together (a branch per chunk made each wait for the one before).
+template <int DC>
+__device__ __forceinline__ void load_qt_operand(const __bf16* __restrict__ Q, int qrow, int N, int h, uint32_t qsign,
+                                                bf16x8 (&qreg)[DC]) {
+  const __bf16* row = Q + (size_t)min(qrow, N - 1) * (16 * DC);
+#pragma unroll
+  for (int c = 0; c < DC; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(row + 16 * c + 8 * h);
+  const bool live = qrow < N;
+#pragma unroll
+  for (int c = 0; c < DC; ++c) qreg[c] = live ? xor_sign(qreg[c], qsign) : zero_bf16x8();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Tile scheduler decode.  The grid is one workgroup per (b*h, tile).  Consecutive workgroup ids
 // are dispatched round-robin over the 8 XCDs (each with its own L2); when B*H is a multiple of 8,

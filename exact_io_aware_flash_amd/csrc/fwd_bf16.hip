@@ -104,10 +104,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void fwd_
   // ---- Q^T operand in registers (B operand: lane holds query q0 + 32w + c32, features 16c + 8h ..)
   const int qrow = q0 + 32 * w + c32;
   bf16x8 qreg[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c)
-    qreg[c] = qrow < N ? xor_sign(*reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + 16 * c + 8 * h), a.qsign)
-                       : zero_bf16x8();
+  load_qt_operand(Q, qrow, N, h, a.qsign, qreg);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -417,10 +414,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pingpong_kernel(FwdArgs a, Sched s
 
   const int qrow = q0 + 32 * w + c32;
   bf16x8 qreg[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c)
-    qreg[c] = qrow < N ? xor_sign(*reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + 16 * c + 8 * h), a.qsign)
-                       : zero_bf16x8();
+  load_qt_operand(Q, qrow, N, h, a.qsign, qreg);
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = zero16();

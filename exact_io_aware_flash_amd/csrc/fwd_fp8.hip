@@ -190,11 +190,63 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
   constexpr int KT = BC * D, VT = D * BC;  // tile bytes
   constexpr int KCH = D / 16;              // 16-byte chunks per K row
   constexpr int KI = KT / 1024 / 4, VI = VT / 1024 / 4;  // copy instructions per wave and tile
+  constexpr int NBUF = 4;
+  // At d = 128 a tile's scales travel with its codes, copied into LDS (4 bytes per key of K,
+  // 4 bytes per feature and 32-key block of V^T: 2 D bytes each, a quarter per wave, so that
+  // every wave issues the same instructions); at d = 64 (2-byte K scale rows, which a 4-byte
+  // copy could not range-check key by key) they are loaded into registers.
+  constexpr bool LS = D == 128;
+  constexpr int SB = 2 * D;  // scale bytes per tile (K and V^T alike)
+  // vector-memory instructions per wave for one tile: the LDS copies and the scale copies/loads
+  constexpr int KOPS = KI + (LS ? 1 : 2), VOPS = VI + 1;
 
+  // four K and four V tile buffers: a tile's copy is issued three steps before its use.  Each
+  // is an array of its own, so that the compiler can tell a read of one buffer from the copies
+  // still in flight into the others (it would otherwise wait for every copy before each read).
   __shared__ __attribute__((aligned(1024))) char kbuf0[KT];
   __shared__ __attribute__((aligned(1024))) char kbuf1[KT];
+  __shared__ __attribute__((aligned(1024))) char kbuf2[KT];
+  __shared__ __attribute__((aligned(1024))) char kbuf3[KT];
   __shared__ __attribute__((aligned(1024))) char vbuf0[VT];
   __shared__ __attribute__((aligned(1024))) char vbuf1[VT];
+  __shared__ __attribute__((aligned(1024))) char vbuf2[VT];
+  __shared__ __attribute__((aligned(1024))) char vbuf3[VT];
+  auto kbuf = [&](auto slot) -> char* {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (r == 0) return kbuf0;
+    else if constexpr (r == 1) return kbuf1;
+    else if constexpr (r == 2) return kbuf2;
+    else return kbuf3;
+  };
+  auto vbuf = [&](auto slot) -> char* {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (r == 0) return vbuf0;
+    else if constexpr (r == 1) return vbuf1;
+    else if constexpr (r == 2) return vbuf2;
+    else return vbuf3;
+  };
+  __shared__ __attribute__((aligned(16))) char ksb0[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char ksb1[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char ksb2[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char ksb3[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char vsb0[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char vsb1[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char vsb2[LS ? SB : 4];
+  __shared__ __attribute__((aligned(16))) char vsb3[LS ? SB : 4];
+  auto ksbuf = [&](auto slot) -> char* {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (r == 0) return ksb0;
+    else if constexpr (r == 1) return ksb1;
+    else if constexpr (r == 2) return ksb2;
+    else return ksb3;
+  };
+  auto vsbuf = [&](auto slot) -> char* {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (r == 0) return vsb0;
+    else if constexpr (r == 1) return vsb1;
+    else if constexpr (r == 2) return vsb2;
+    else return vsb3;
+  };
   __shared__ unsigned short blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int bcount;
 
@@ -236,25 +288,25 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
   i32x8 qop[DF];
   int qsc = 0;
   {
-    const uint8_t* qr = a.q8 + ((size_t)bh * N + qrow) * D;
+    // rows past N load row N - 1 and are zeroed after: no branch around the loads, so they are
+    // all in flight together
+    const bool live = qrow < N;
+    const size_t qr_row = (size_t)bh * N + min(qrow, N - 1);
+    const uint8_t* qr = a.q8 + qr_row * D;
+    const uint8_t* qs = a.qs + qr_row * NSB;
+    const uint32_t srow = NSB == 4 ? *reinterpret_cast<const uint32_t*>(qs) : *reinterpret_cast<const unsigned short*>(qs);
+    // a negative scale flips the sign bit of every Q code (exact), the exponent uses |scale|
+    const uint32_t m = a.qsign;
 #pragma unroll
     for (int f = 0; f < DF; ++f) {
-      uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi4 = lo;
-      if (qrow < N) {
-        lo = *reinterpret_cast<const uint4*>(qr + 64 * f + 16 * h);
-        hi4 = *reinterpret_cast<const uint4*>(qr + 64 * f + 32 + 16 * h);
-      }
-      // a negative scale flips the sign bit of every Q code (exact), the exponent uses |scale|
-      const uint32_t m = a.qsign;
-      lo.x ^= m; lo.y ^= m; lo.z ^= m; lo.w ^= m;
-      hi4.x ^= m; hi4.y ^= m; hi4.z ^= m; hi4.w ^= m;
+      uint4 lo = *reinterpret_cast<const uint4*>(qr + 64 * f + 16 * h);
+      uint4 hi4 = *reinterpret_cast<const uint4*>(qr + 64 * f + 32 + 16 * h);
+      lo.x = live ? lo.x ^ m : 0u; lo.y = live ? lo.y ^ m : 0u; lo.z = live ? lo.z ^ m : 0u; lo.w = live ? lo.w ^ m : 0u;
+      hi4.x = live ? hi4.x ^ m : 0u; hi4.y = live ? hi4.y ^ m : 0u;
+      hi4.z = live ? hi4.z ^ m : 0u; hi4.w = live ? hi4.w ^ m : 0u;
       qop[f] = join16x2(lo, hi4);
     }
-    if (qrow < N) {
-      const uint8_t* s = a.qs + ((size_t)bh * N + qrow) * NSB;
-      const uint32_t row = NSB == 4 ? *reinterpret_cast<const uint32_t*>(s) : *reinterpret_cast<const unsigned short*>(s);
-      qsc = (int)(row >> (8 * h));  // byte 2f: block 2f + h
-    }
+    qsc = live ? (int)(srow >> (8 * h)) : 0;  // byte 2f: block 2f + h
   }
 
   f32x16 oacc[DB];
@@ -317,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
       const int off = (k0 + 32 * kb + pi32(c32)) * NSB;
       const uint32_t row = NSB == 4 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ks_r, off, 0, 0)
                                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks_r, off, 0, 0);
-      out[kb] = (int)(row >> (8 * h));
+      out[kb] = (int)row;  // shifted by 8 h where used (a shift here would wait for the load)
     }
   };
   auto load_vsc = [&](int k0) -> int {
@@ -325,6 +377,24 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     return DB == 4 ? (int)__builtin_amdgcn_raw_buffer_load_b32(vs_r, off, 0, 0)
                    : (int)(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vs_r, off, 0, 0);
   };
+  // LDS scale copy (d = 128): wave w copies bytes [SB/4 w, SB/4 (w + 1)) of the tile's scales,
+  // starting at byte byte0 of the head's array, 4 bytes per lane (keys past N read as zero)
+  auto copy_scales = [&](const Rsrc& r, char* dst, int byte0) {
+    constexpr int PW = SB / 4;
+#ifdef FA_CHECK
+    if (lane < PW / 4) *reinterpret_cast<uint32_t*>(dst + PW * w + 4 * lane) = 0xFFFFFFFFu;  // NaN scale
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+    if (lane < PW / 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(dst + PW * w), 4, byte0 + PW * w + 4 * lane, 0, 0, 0);
+  };
+  // the scales of a tile in slot r as the MFMAs take them: K rows of the two 32-key blocks
+  // shifted so that byte 2f is block 2f + h; V^T: the DB bytes of feature 32 db + c32 (db = byte)
+  // in key block h of the tile
+  auto lds_ksc = [&](const char* src, int kb) -> int {
+    return (int)(*reinterpret_cast<const uint32_t*>(src + (32 * kb + pi32(c32)) * 4) >> (8 * h));
+  };
+  auto lds_vsc = [&](const char* src) -> int { return *reinterpret_cast<const int*>(src + (32 * h + c32) * 4); };
 
   // S^T for the two 32-key blocks of a tile: register r of lane half h = key k0 + 32 kb + 16 h + r
   auto scores = [&](const char* tk, const int (&ksc)[2], f32x16(&s)[2]) {
@@ -361,55 +431,90 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     m = m_new;
   };
 
-  // Software pipeline (as the bf16 kernel): K copies and K scales two tiles ahead, V copies and
-  // V scales one tile ahead; the scores one tile ahead of the exponentials.
+  // Software pipeline: the scores one tile ahead of the exponentials, as in the bf16 kernel, but
+  // the copies run further ahead, since a 64-key FP8 step holds half the matrix work of a bf16
+  // one while a copy takes as long to land.  Tile i (its K and V copies and their scale loads)
+  // lives in buffer slot i % 4.  Step t reads K[t+1] and V[t]; it issues K[t+4] and V[t+3] and
+  // ends by waiting for K[t+2] and V[t+1] (issued in step t-2), so each copy has two steps to
+  // land.  Vector-memory instructions complete in issue order, so that wait is a count: the
+  // instructions of steps t-1 and t may stay in flight.
   f32x16 sbuf[2][2];
-  // scale registers: at step t, ksc[t % 2] holds tile t+1 and ksc[(t + 1) % 2] receives tile
-  // t+2 (ksc[2] holds tile 0); vsc[t % 2] holds tile t and vsc[(t + 1) % 2] receives tile t+1
-  int ksc[3][2] = {{kP8Scale, kP8Scale}, {kP8Scale, kP8Scale}, {kP8Scale, kP8Scale}};
-  int vsc[2] = {kP8Scale, kP8Scale};
-  float alpha = 1.f;
-  if (ntiles > 0) {
-    issue_k(kbuf0, tile_start(0));
-    issue_v(vbuf0, tile_start(0));
-    load_ksc(tile_start(0), ksc[2]);
-    vsc[0] = load_vsc(tile_start(0));
-    if (ntiles > 1) {
-      issue_k(kbuf1, tile_start(1));
-      load_ksc(tile_start(1), ksc[0]);
-    }
+  int ksc[NBUF][2];
+  int vsc[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) {
+    ksc[i][0] = ksc[i][1] = kP8Scale;
+    vsc[i] = kP8Scale;
   }
+  auto issue_ktile = [&](int i, auto slot) {
+    constexpr int r = decltype(slot)::value;
+    const int k0 = tile_start(i);
+    issue_k(kbuf(slot), k0);
+    if constexpr (LS)
+      copy_scales(ks_r, ksbuf(slot), k0 * NSB);
+    else
+      load_ksc(k0, ksc[r]);
+  };
+  auto issue_vtile = [&](int i, auto slot) {
+    constexpr int r = decltype(slot)::value;
+    const int k0 = tile_start(i);
+    issue_v(vbuf(slot), k0);
+    if constexpr (LS)
+      copy_scales(vs_r, vsbuf(slot), k0 * DB);
+    else
+      vsc[r] = load_vsc(k0);
+  };
+  // scales of the tile in slot r, as the MFMAs take them
+  auto kscales = [&](auto slot, int (&out)[2]) {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (LS) {
+      out[0] = lds_ksc(ksbuf(slot), 0);
+      out[1] = lds_ksc(ksbuf(slot), 1);
+    } else {
+      out[0] = ksc[r][0] >> (8 * h);
+      out[1] = ksc[r][1] >> (8 * h);
+    }
+  };
+  auto vscale = [&](auto slot) -> int {
+    constexpr int r = decltype(slot)::value;
+    if constexpr (LS)
+      return lds_vsc(vsbuf(slot));
+    else
+      return vsc[r];
+  };
+  float alpha = 1.f;
+  if (ntiles > 0) issue_ktile(0, IC<0>{}), issue_vtile(0, IC<0>{});
+  if (ntiles > 1) issue_ktile(1, IC<1>{}), issue_vtile(1, IC<1>{});
+  if (ntiles > 2) issue_ktile(2, IC<2>{}), issue_vtile(2, IC<2>{});
+  if (ntiles > 3) issue_ktile(3, IC<3>{});
   wait_dma();
   __syncthreads();
   if (ntiles > 0) {
-    scores(kbuf0, ksc[2], sbuf[0]);
+    int ksc0[2];
+    kscales(IC<0>{}, ksc0);
+    scores(kbuf(IC<0>{}), ksc0, sbuf[0]);
     mask_tile(sbuf[0], tile_start(0));
     update_max(sbuf[0], m_used, alpha);
     alpha = 1.f;  // nothing accumulated yet
   }
-  // every wave has read K[0] before step 0 copies K[2] over it
-  if (ntiles > 2) lds_barrier();
+  // every wave has read K[0] before step 0 copies K[4] over it
+  if (ntiles > 4) lds_barrier();
 
-  auto step = [&](int t, auto parity) {
-    constexpr int par = decltype(parity)::value;  // t % 2
-    char* const k_next = par ? kbuf0 : kbuf1;      // holds K[t+1] (stale K on the last tile)
-    char* const k_free = par ? kbuf1 : kbuf0;      // held K[t]; receives K[t+2]
-    char* const v_cur = par ? vbuf1 : vbuf0;       // holds V[t]
-    char* const v_free = par ? vbuf0 : vbuf1;      // held V[t-1]; receives V[t+1]
+  auto step = [&](int t, auto slot) {
+    constexpr int r = decltype(slot)::value;  // t % 4
+    constexpr int par = r & 1;                // t % 2
+    // K[t+1] (stale K on the last tile: in bounds, result discarded) and its scales; V[t]
+    const char* const k_next = kbuf(IC<(r + 1) % NBUF>{});
+    int ksc_next[2];
+    kscales(IC<(r + 1) % NBUF>{}, ksc_next);
+    const char* const v_cur = vbuf(IC<r>{});
+    const int vsc_cur = vscale(IC<r>{});
     f32x16(&s_cur)[2] = sbuf[par];
     f32x16(&s_nxt)[2] = sbuf[par ^ 1];
-    int(&ksc_next)[2] = ksc[par];      // K scales of tile t+1
-    int(&ksc_free)[2] = ksc[par ^ 1];  // receives tile t+2
-    const int vsc_cur = vsc[par];
-    const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles;
-    if (has2) {
-      issue_k(k_free, tile_start(t + 2));
-      load_ksc(tile_start(t + 2), ksc_free);
-    }
-    if (has1) {
-      issue_v(v_free, tile_start(t + 1));
-      vsc[par ^ 1] = load_vsc(tile_start(t + 1));
-    }
+    const bool has1 = t + 1 < ntiles, has2 = t + 2 < ntiles, has3 = t + 3 < ntiles, has4 = t + 4 < ntiles;
+    // K[t+4] into the slot of K[t] (read in step t-1), V[t+3] into that of V[t-1] (step t-1)
+    if (has4) issue_ktile(t + 4, IC<r>{});
+    if (has3) issue_vtile(t + 3, IC<(r + 3) % NBUF>{});
 
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
@@ -495,13 +600,23 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
       m_used = has1 ? m_nx : m_used;
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_dma();
-    __syncthreads();
+    // K[t+2] and V[t+1] have landed once at most the instructions of steps t-1 and t remain
+    if (has4)
+      wait_vm<2 * KOPS + 2 * VOPS>();
+    else if (has3)
+      wait_vm<KOPS + 2 * VOPS>();
+    else if (has2)
+      wait_vm<VOPS>();
+    else
+      wait_vm<0>();
+    lds_barrier();
   };
 
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < ntiles; t += 4) {
     step(t, IC<0>{});
     if (t + 1 < ntiles) step(t + 1, IC<1>{});
+    if (t + 2 < ntiles) step(t + 2, IC<2>{});
+    if (t + 3 < ntiles) step(t + 3, IC<3>{});
   }
 
   // ---- epilogue: lane holds features 32 db + 8 g + 4 h + e of query qrow in register 4 g + e
