@@ -452,19 +452,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   odma.init(w, lane);
   // LSE and D of the next tile: loaded when its copy starts, used only when stored (at the end
   // of the tile), so that no wait on the loads holds up the copies issued before them
+  // (by the first two P waves only; rows past N load row N - 1 and are replaced when stored, so
+  // that nothing right after the loads waits for them)
   float lraw = 0.f, draw = 0.f;
+  bool rlive = false;
   auto rowstats_load = [&](int q0) {
-    if (tid < BQ) {
+    if (!dsw && tid < BQ) {
       const int qr = q0 + tid;
-      lraw = qr < N ? a.lse[rbase + qr] : neg_inf();
-      draw = qr < N ? a.delta[rbase + qr] : 0.f;
+      rlive = qr < N;
+      const size_t r = rbase + min(qr, N - 1);
+      lraw = a.lse[r];
+      draw = a.delta[r];
     }
   };
   auto rowstats_store = [&](int buf) {
-    if (tid < BQ) {
+    if (!dsw && tid < BQ) {
       // rows past N, or rows that see no key, get +inf so that P = 0
-      lbuf[buf][tid] = (lraw == neg_inf()) ? __builtin_huge_valf() : lraw * kLog2e;
-      dbuf[buf][tid] = draw;
+      lbuf[buf][tid] = (!rlive || lraw == neg_inf()) ? __builtin_huge_valf() : lraw * kLog2e;
+      dbuf[buf][tid] = rlive ? draw : 0.f;
     }
   };
 
@@ -553,7 +558,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
 
   // copy of tile t + 1 into the other buffers (from phase 2 of tile t, once no wave reads tile
   // t - 1 any more), by all waves
-  auto prefetch = [&](int t, int buf) {
+  // (the buffer is a compile-time choice: copies into an LDS address the compiler cannot place
+  // make it wait for them before every later LDS read)
+  auto prefetch = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int qn = tile_start(t + 1);
     qdma.issue(Qh, N, buf ? qbuf1 : qbuf0, qn, w);
     odma.issue(Oh, N, buf ? obuf1 : obuf0, qn, w);
@@ -589,8 +597,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
   // 16 i + k holds the value of row 16 (k / 8) + 8 (i / 2) + k % 8 of the part, and a DPP row
   // broadcast of lane k within each row of 16 lanes then gives every lane of half h the value of
   // score element r = k (row 16 (r / 8) + 8h + r % 8).
+  // (the lane's byte offset is formed once, so that each read is the array plus two offsets: a
+  // longer chain of address steps loses the compiler's knowledge of which LDS array is read, and
+  // it then waits for every copy into LDS in flight before the read)
+  const int stat_off = 4 * (16 * ((lane & 15) >> 3) + 8 * h + (lane & 7));
   auto stat_load = [&](const float* rows, int s) -> float {
-    return rows[32 * s + 16 * ((lane & 15) >> 3) + 8 * h + (lane & 7)];
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(rows) + 128 * s + stat_off);
   };
   auto stat_of = [](float v, int r) __attribute__((always_inline)) -> float { return row_bcast(v, r); };
   if (!dsw) {
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
       const bool mask = tile_mask(q0);
 #pragma unroll
       for (int s = 0; s < NH; ++s) {
-        if (s == 2 && has_next) prefetch(t, par ^ 1);
+        if (s == 2 && has_next) prefetch(t, std::integral_constant<int, par ^ 1>{});
         if (s > 0)
           p_phase(std::true_type{}, std::true_type{}, tq, s, mask, q0 + 32 * s, to, lbuf[par], s - 1);
         else if (!FIRST)
@@ -729,7 +741,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdArgs a, Sched sc) {
       const bool has_next = t + 1 < ntiles;
 #pragma unroll
       for (int s = 0; s < NH; ++s) {
-        if (s == 2 && has_next) prefetch(t, par ^ 1);
+        if (s == 2 && has_next) prefetch(t, std::integral_constant<int, par ^ 1>{});
         if (s >= 2)
           ds_phase(std::true_type{}, std::true_type{}, to, s - 1, tq, dbuf[par], s - 2);
         else if (s == 1) {
