@@ -1398,11 +1398,11 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int nkv = (a.N + 127) / 128;
   if constexpr (D == 64) {
     static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_wave_kernel<D, C, S>), 256);
-    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots, /*uneven=*/C || S);
     hipLaunchKernelGGL((bwd_dkdv_wave_kernel<D, C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc);
   } else {
     static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, C, S>), 512);
-    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+    const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots, /*uneven=*/C || S);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, C, S>), dim3(nkv * a.BH), dim3(512), 0, st, a, sc);
   }
   return hipGetLastError();
@@ -1412,7 +1412,7 @@ template <int D, bool C, bool S>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nq = (a.N + 127) / 128;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dq_kernel<D, C, S>));
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
@@ -1442,7 +1442,7 @@ template <bool C, bool S>
 hipError_t launch_fused_t(const BwdArgs& a, float* dq_acc, hipStream_t st) {
   const int nkv = (a.N + 127) / 128;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_fused_kernel<C, S>), 256);
-  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots);
+  const Sched sc = make_sched(nkv, a.BH, /*heavy_last_tile=*/0, slots, /*uneven=*/C || S);
   hipLaunchKernelGGL((bwd_fused_kernel<C, S>), dim3(nkv * a.BH), dim3(256), 0, st, a, sc, dq_acc);
   return hipGetLastError();
 }

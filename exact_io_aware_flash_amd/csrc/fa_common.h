@@ -257,8 +257,9 @@ __device__ __forceinline__ void load_qt_operand(const __bf16* __restrict__ Q, in
 //    of work, so the long tiles must start first), or
 //  - head-major: one head after another, each heaviest tile first, so that the workgroups in
 //    flight on an XCD stream the same head's K/V tiles at about the same time and share them in
-//    L2 (used when a head has enough tiles to fill the XCD's slots twice over, where the late
-//    start of the last head's long tiles is a small tail).
+//    L2 (always when a head's tiles carry equal work; with the causal triangle or a block mask,
+//    once a head has enough tiles to fill the XCD's slots, where the late start of the last
+//    head's long tiles is a small tail; see make_sched).
 // ---------------------------------------------------------------------------------------------
 struct Sched {
   int ntiles;      // tiles per head

@@ -658,7 +658,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int BR = 32 * NW;
   const int nq = (a.N + BR - 1) / BR;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S, false, NW>), 64 * NW);
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C && !S);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S, /*alternate=*/C && !S);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S, false, NW>), dim3(nq * a.BH), dim3(64 * NW), 0, st, a, sc);
   return hipGetLastError();
 }
@@ -667,7 +667,7 @@ template <bool C>
 static hipError_t launch_pingpong_t(const FwdArgs& a, hipStream_t st) {
   const int nq = (a.N + 255) / 256;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_pingpong_kernel<C>), 512);
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C, /*alternate=*/C);
   hipLaunchKernelGGL((fwd_pingpong_kernel<C>), dim3(nq * a.BH), dim3(512), 0, st, a, sc);
   return hipGetLastError();
 }
@@ -691,7 +691,7 @@ static hipError_t launch_splitkv_t(const FwdArgs& a, hipStream_t st) {
   constexpr int BR = 128;
   const int nq = (a.N + BR - 1) / BR;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, C, S, true>));
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, C, S, true>), dim3(nq * a.BH, a.splits), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }

@@ -644,7 +644,7 @@ static hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t st) {
   constexpr int BR = 128;
   const int nq = (a.N + BR - 1) / BR;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&fwd_mxfp8_kernel<D, C, S>));
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*alternate=*/C && !S);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S, /*alternate=*/C && !S);
   hipLaunchKernelGGL((fwd_mxfp8_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
