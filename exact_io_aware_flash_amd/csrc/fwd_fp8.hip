@@ -500,6 +500,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
   // every wave has read K[0] before step 0 copies K[4] over it
   if (ntiles > 4) lds_barrier();
 
+  // P[t] as E4M3 codes, the PV operand (kept across steps: each word's first conversion keeps
+  // the half it does not write)
+  i32x8 pop = {0, 0, 0, 0, 0, 0, 0, 0};
   auto step = [&](int t, auto slot) {
     constexpr int r = decltype(slot)::value;  // t % 4
     constexpr int par = r & 1;                // t % 2
@@ -531,7 +534,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     // is register r of block kb.  Each MFMA is followed by a share of the exponentials.
     constexpr int NS = 2 * DF;
     constexpr int EPS = 32 / NS;
-    i32x8 pop;
     {
       s_nxt[0] = zero16();
       s_nxt[1] = zero16();
@@ -548,7 +550,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
 #pragma unroll
         for (int e = 0; e < EPS; e += 4) {
           const int j = i * EPS + e;
-          int r = __builtin_amdgcn_cvt_pk_fp8_f32(s_cur[j >> 4][j & 15], s_cur[j >> 4][(j & 15) + 1], 0, false);
+          // the first conversion fills the low half of the word and keeps the rest of its old value
+          // (the previous tile's, overwritten by the second one): no zeroing move
+          int r = __builtin_amdgcn_cvt_pk_fp8_f32(s_cur[j >> 4][j & 15], s_cur[j >> 4][(j & 15) + 1], pop[j >> 2], false);
           r = __builtin_amdgcn_cvt_pk_fp8_f32(s_cur[j >> 4][(j & 15) + 2], s_cur[j >> 4][(j & 15) + 3], r, true);
           pop[j >> 2] = r;
         }

@@ -80,13 +80,25 @@ def test_long_context_64k_forward_every_tile(dev):
 
 
 def test_head_major_schedule_sampled(dev):
-    """B*H = 16 heads of N = 8192, d = 128, causal: the dK/dV grid has enough key tiles per head to
-    run its XCD groups head by head, while the forward and dQ grids run tile level by tile level."""
+    """B*H = 16 heads of N = 8192, d = 128, causal: two heads per XCD group, each with as many
+    tiles as the XCD holds workgroups or more, so every grid runs head by head, and the forward
+    alternates its key direction by cohort."""
     t = workloads.random_case(2, 8, 8192, 128, "bf16", seed=900)
     rows = G.sample_rows(8192, 40, seed=901)
     cols = G.sample_rows(8192, 40, seed=902)
     _run_and_compare("head-major N=8192 d=128", t, 1.0 / math.sqrt(128), True, dev, heads=[(0, 0), (1, 7)],
                      rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_major_equal_tiles_sampled(dev, d):
+    """Non-causal heads whose tiles carry equal work run head by head even when a head has fewer
+    tiles than the XCD holds workgroups: B*H = 16 heads of N = 2048 (8 to 16 tiles per head)."""
+    t = workloads.random_case(2, 8, 2048, d, "bf16", seed=910 + d)
+    rows = G.sample_rows(2048, 40, seed=911)
+    cols = G.sample_rows(2048, 40, seed=912)
+    _run_and_compare(f"head-major equal tiles N=2048 d={d}", t, 1.0 / math.sqrt(d), False, dev,
+                     heads=[(0, 0), (0, 5), (1, 2), (1, 7)], rows=rows, cols=cols)
 
 
 def test_block_sparse(dev):
