@@ -222,6 +222,37 @@ def test_invariants_on_device_outputs(dev):
         assert np.abs(G.host_f64(dk)[0, 0].sum(0)).max() < 0.05 * math.sqrt(N), "sum_j dK_j = 0"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_dominant_score_on_device_outputs(dev, causal):
+    """Second witness on the device results (one-hot dominant row): with Q_i = 10 K_j* for one
+    visible key j* per row, the score of j* exceeds every other visible score by tens of nats, so
+    O_i = V_j* (up to the bf16 rounding of P and of O) and LSE_i = scale Q_i K_j* (the other keys
+    add about e^-40 to the sum).  Several tiles, a ragged tail, d = 128."""
+    import torch
+
+    import exact_io_aware_flash_amd as fa
+
+    N, d = 300, 128
+    scale = 1.0 / math.sqrt(d)
+    t = workloads.random_case(1, 1, N, d, "bf16", seed=520, with_do=False)
+    rng = np.random.default_rng(521)
+    jstar = np.array([rng.integers(0, i + 1) if causal else rng.integers(0, N) for i in range(N)])
+    # Q_i = 10 K_j*, rounded to bf16 (the inputs are bf16 bit patterns); the reference reads the
+    # device copy back
+    t.q[0, 0] = workloads.round_to_bf16_bits(10.0 * workloads.bf16_bits_to_f32(t.k[0, 0, jstar]))
+    q, k, v = (G.to_dev(x, "bf16", dev) for x in (t.q, t.k, t.v))
+    o, lse = fa.fwd(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    qh, kh, vh = (G.host_f64(x)[0, 0] for x in (q, k, v))
+    s = scale * qh @ kh.T
+    if causal:
+        s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    gap = s[np.arange(N), jstar] - np.max(np.where(np.eye(N, dtype=bool)[jstar], -np.inf, s), axis=1)
+    assert gap.min() > 40.0, gap.min()  # the construction holds (causal row 0 sees one key: gap inf)
+    G.check(f"dominant row O causal={causal}", G.host_f64(o)[0, 0], vh[jstar], G.TOL_BF16, True)
+    G.check(f"dominant row LSE causal={causal}", G.host_f64(lse)[0, 0], s[np.arange(N), jstar], G.TOL_LSE, False)
+
+
 def test_bitwise_reproducible(dev):
     import torch
 
