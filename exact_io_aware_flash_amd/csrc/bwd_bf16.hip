@@ -827,23 +827,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Sched sc) {
     ntiles = 2 * cnt;
     if (cnt > 0 && (int)blist[cnt - 1] * kMaskBlock + BC >= N) ntiles -= 1;
   }
+  // causal query tiles of alternate cohorts walk the keys from the diagonal down
+  // (sched_descending, as in the forward); the masks depend only on each tile's first key
+  const bool desc = CAUSAL && !SPARSE && sched_descending(sc, gridDim.x);
   auto tile_start = [&](int t) -> int {
     if (SPARSE) return (int)blist[t >> 1] * kMaskBlock + (t & 1) * BC;
-    return t * BC;
+    return (desc ? ntiles - 1 - t : t) * BC;
   };
 
   const int qrow = q0 + 32 * w + c32;
+  // Q (sign of the scale folded in) and dO rows in registers; rows past N load row N - 1 and are
+  // zeroed, with no branch around the loads
   bf16x8 qreg[DC], doreg[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    if (qrow < N) {
-      qreg[c] = xor_sign(*reinterpret_cast<const bf16x8*>(a.q + base + (size_t)qrow * D + 16 * c + 8 * h), a.ssign);
-      doreg[c] = *reinterpret_cast<const bf16x8*>(a.dout + base + (size_t)qrow * D + 16 * c + 8 * h);
-    } else {
-      qreg[c] = zero_bf16x8();
-      doreg[c] = zero_bf16x8();
-    }
-  }
+  load_qt_operand(a.q + base, qrow, N, h, a.ssign, qreg);
+  load_qt_operand(a.dout + base, qrow, N, h, 0u, doreg);
   float lse2 = __builtin_huge_valf(), dval = 0.f;
   if (qrow < N) {
     const float l = a.lse[rbase + qrow];
@@ -1412,7 +1409,7 @@ template <int D, bool C, bool S>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nq = (a.N + 127) / 128;
   static const int slots = xcd_slots(reinterpret_cast<const void*>(&bwd_dq_kernel<D, C, S>));
-  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S);
+  const Sched sc = make_sched(nq, a.BH, /*heavy_last_tile=*/1, slots, /*uneven=*/C || S, /*alternate=*/C && !S);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C, S>), dim3(nq * a.BH), dim3(256), 0, st, a, sc);
   return hipGetLastError();
 }
