@@ -161,6 +161,31 @@ def test_negative_scale_long_sampled(dev):
                      rows=rows, cols=cols)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mult", [16.0, 64.0])
+def test_sharp_softmax_forward(dev, d, mult):
+    """Scores far larger than the workloads' (scale = mult / sqrt(d), both signs): most rows are
+    close to one-hot, LSE reaches a few hundred, and the running maximum moves past the rescale
+    threshold many times along a row. Forward only, against the oracle at the stated bars: the
+    bf16 backward rounds dS, whose error grows with the scores and leaves the stated bar at such
+    scales (an error budget of the rounding alone, not of the kernels)."""
+    for i, (causal, dens, sign) in enumerate(((False, None, 1.0), (True, None, -1.0), (False, 0.5, 1.0))):
+        t = workloads.random_case(1, 2, 700, d, "bf16", seed=2300 + 10 * i + d, with_do=False, mask_density=dens)
+        _run_and_compare(f"sharp softmax x{mult:g} d={d} causal={causal} mask={dens}", t, sign * mult / math.sqrt(d),
+                         causal, dev, heads=[(0, 0), (0, 1)], backward=False)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_flat_softmax(dev, d, causal):
+    """scale = 1e-3: every row nearly uniform over the keys it sees (LSE close to the log of their
+    count, P close to its mean everywhere), forward and backward."""
+    t = workloads.random_case(1, 2, 700, d, "bf16", seed=2400 + d + int(causal))
+    _run_and_compare(f"flat softmax d={d} causal={causal}", t, 1e-3, causal, dev, heads=[(0, 0), (0, 1)])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_dead_rows(dev, dtype, d):
