@@ -534,14 +534,27 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     // is register r of block kb.  Each MFMA is followed by a share of the exponentials.
     constexpr int NS = 2 * DF;
     constexpr int EPS = 32 / NS;
+    // operands read two MFMAs ahead: K for this section, and V for the first two PV MFMAs of
+    // section 2 in this section's last slots (an LDS read takes longer than one MFMA)
+    auto kread = [&](int i) {
+      const int f = i >> 1, kb = i & 1;
+      return join16x2(lds16(k_next + koff[kb][f][0]), lds16(k_next + koff[kb][f][1]));
+    };
+    auto vread = [&](int db) { return join16x2(lds16(v_cur + voff[db][0]), lds16(v_cur + voff[db][1])); };
+    i32x8 kop[NS], vop[DB];
     {
       s_nxt[0] = zero16();
       s_nxt[1] = zero16();
+      kop[0] = kread(0);
+      kop[1] = kread(1);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int f = i >> 1, kb = i & 1;
-        const i32x8 kop = join16x2(lds16(k_next + koff[kb][f][0]), lds16(k_next + koff[kb][f][1]));
-        s_nxt[kb] = mfma_mx_sel(2 * f, 2 * f, kop, qop[f], s_nxt[kb], ksc_next[kb], qsc);
+        if (i + 2 < NS)
+          kop[i + 2] = kread(i + 2);
+        else
+          vop[i + 2 - NS] = vread(i + 2 - NS);  // V[t] landed before this step
+        s_nxt[kb] = mfma_mx_sel(2 * f, 2 * f, kop[i], qop[f], s_nxt[kb], ksc_next[kb], qsc);
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
           const int j = i * EPS + e;
@@ -570,17 +583,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mxfp8_kernel(Fp8FwdArgs a, Sched s
     __builtin_amdgcn_s_setprio(1);
     // section 2: O^T += V^T P^T over the 64 keys, the row sums of P[t], the max after S[t+1].
     // Written out slot by slot like section 1: each PV MFMA is followed by its share of the row
-    // sums and of the running max (V operands read one MFMA ahead).
+    // sums and of the running max (V operands read two MFMAs ahead, the first two in section 1).
     {
       constexpr int EPD = 32 / DB;  // elements per slot
       float part[4] = {0.f, 0.f, 0.f, 0.f};
       float mt = s_nxt[0][0];
-      auto vread = [&](int db) { return join16x2(lds16(v_cur + voff[db][0]), lds16(v_cur + voff[db][1])); };
-      i32x8 vop[DB];
-      vop[0] = vread(0);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        if (db + 1 < DB) vop[db + 1] = vread(db + 1);
+        if (db + 2 < DB) vop[db + 2] = vread(db + 2);
         oacc[db] = mfma_mx_sel(db, 0, vop[db], pop, oacc[db], vsc_cur, kP8Scale);
 #pragma unroll
         for (int e = 0; e < EPD; ++e) {
