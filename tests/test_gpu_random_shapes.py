@@ -1,7 +1,7 @@
 """GPU parity on seeded random shapes: B, H, ragged N, head dimension, dtype, causal flag, a
-random 128 x 128 block mask and the scale all drawn from one generator, forward and backward of
-every head compared with the fp64 oracle at the same tolerances as the other parity tests.  The
-sizes stay small enough that the oracle finishes each case in well under a second."""
+random 128 x 128 block mask and the scale (both signs) drawn from seeded generators, forward and
+backward of every head compared with the fp64 oracle at the same tolerances as the other parity
+tests.  The sizes stay small enough that the oracle finishes each case in well under a second."""
 import math
 
 import numpy as np
@@ -12,7 +12,7 @@ from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = 48
 
 
 def _draw(i):
@@ -26,6 +26,8 @@ def _draw(i):
     causal = bool(rng.random() < 0.5)
     masked = bool(rng.random() < 0.4)
     scale = float(rng.uniform(0.3, 1.5)) / math.sqrt(d)
+    if np.random.default_rng(7000 + i).random() < 0.5:  # a generator of its own: the draws above stay as they were
+        scale = -scale
     return B, H, N, d, dtype, causal, masked, scale
 
 
