@@ -217,3 +217,22 @@ def test_fwd_mxfp8_remapped_grid(dev):
     # B*H = 16 (remapped grid, level order), d = 64, non-causal, every row compared on 2 heads
     t = workloads.random_case(2, 8, 1024, 64, "bf16", seed=3201, with_do=False)
     _fp8_case("remapped grid", t, 0.125, False, dev, [(0, 3), (1, 6)])
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_fwd_mxfp8_random_shape(dev, i):
+    # seeded random shapes: B, H, ragged N, d, causal flag, a random block mask and a scale of
+    # either sign, every head against the oracle within the P-rounding bound
+    rng = np.random.default_rng(5000 + i)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    N = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 300)), int(rng.integers(300, 700))]))
+    d = int(rng.choice([64, 128]))
+    causal, masked = bool(rng.random() < 0.5), bool(rng.random() < 0.4)
+    scale = float(rng.uniform(0.3, 1.5)) / np.sqrt(d) * (1 if rng.random() < 0.5 else -1)
+    t = workloads.random_case(B, H, N, d, "bf16", seed=5100 + i, with_do=False,
+                              mask_density=0.5 if masked else None, mask_seed=5200 + i)
+    if t.block_mask is not None:
+        np.fill_diagonal(t.block_mask, 1)  # every query block keeps at least its own keys
+    worst = _fp8_case(f"random {i}: N={N} d={d} scale={scale:.4f}", t, scale, causal, dev,
+                      [(b, h) for b in range(B) for h in range(H)])
+    assert worst <= 1.0
